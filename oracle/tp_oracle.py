@@ -1,0 +1,203 @@
+"""Oracle for the tensor-parallel sharded linear layer Y = X W (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module; the product path (the
+HIP library and its Python binding) never does, and this module imports
+nothing from it.
+
+Everything here is plain float64 numpy, computed shard by shard in the order
+the tensor-parallelism pages describe, so that the split, concatenation and
+summation steps are themselves checked and not only the final product.
+Inputs are the exact values the GPU receives (bfloat16 or float32 values held
+in float32 arrays); they are widened to float64 before any arithmetic.
+The one library primitive used as a step is the float64 matrix product
+``numpy.matmul``; the Gaussian error function comes from ``scipy.special.erf``.
+
+Sources (the web pages on tensor parallelism this library implements):
+  [TP-topic]   "Tensor Parallelism" topic page, chipfoundryservices.com
+  [AI-gloss]   "Tensor Parallelism" entry, AI Glossary, aiforbusinessandlife.com
+  [DLwPT]      "Tensor parallelism" concept page, Deep Learning with PyTorch 2e (liveBook)
+
+Pins (tests/test_oracle.py): the worked example of [AI-gloss] "Worked example"
+(fixture tests/golden/worked_example.json), brute force against pure-Python
+loops on small integer inputs, the split invariants for every shard count
+dividing the split dimension, textbook values of the normal CDF for GeLU and
+an independent Taylor-series error function, and mutation tests that plant
+plausible mistakes here and check that a pin catches each one.
+Readings where the pages are silent: W is [in, out] row-major and Y = X W;
+blocks are contiguous and shard s takes the s-th; N must divide the split
+dimension; the MLP activation is the exact GeLU x * Phi(x); the intermediate
+H is kept in float64 here (the GPU rounds it to bfloat16); partial sums are
+added in ascending shard order.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "widen",
+    "matmul",
+    "col_block",
+    "row_block",
+    "x_block",
+    "concat_cols",
+    "reduce_sum",
+    "gelu",
+    "apply_act",
+    "col_shard_outputs",
+    "col_linear",
+    "row_partials",
+    "row_linear",
+    "mlp_shard_partials",
+    "mlp",
+]
+
+ACTS = ("none", "gelu")
+
+
+def widen(a) -> np.ndarray:
+    """Exact widening of the received values (float32 / bfloat16 held in float32) to float64."""
+    return np.asarray(a, dtype=np.float64)
+
+
+def matmul(a, b) -> np.ndarray:
+    """C[m, n] = sum_k A[m, k] * B[k, n] in float64.
+
+    The definition of the matrix product named by [DLwPT] "Related concepts"
+    (entries of the result are sums of products of rows of the first factor
+    with columns of the second); the float64 library product is the step.
+    """
+    a = widen(a)
+    b = widen(b)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"matmul shape mismatch {a.shape} x {b.shape}")
+    return a @ b
+
+
+def _check_split(dim: int, n: int, what: str) -> int:
+    """Even split only: each shard owns dim / n contiguous indices ([TP-topic] figure, '[d, d/N]')."""
+    if n < 1 or dim % n != 0:
+        raise ValueError(f"{what}: {n} shards do not evenly divide {dim}")
+    return dim // n
+
+
+def col_block(w, n: int, s: int) -> np.ndarray:
+    """W_s of the column-wise split W = [W_1, ..., W_N]: columns s*Nout/N .. (s+1)*Nout/N - 1.
+
+    [TP-topic] "Column-Wise Parallelism"; [AI-gloss] "How it works" (split W by output columns).
+    """
+    w = np.asarray(w)
+    width = _check_split(w.shape[1], n, "column split")
+    return w[:, s * width:(s + 1) * width]
+
+
+def row_block(w, n: int, s: int) -> np.ndarray:
+    """W_s of the row-wise split W = [W_1; ...; W_N]: rows s*K/N .. (s+1)*K/N - 1.
+
+    [TP-topic] "Row-Wise Parallelism" (W stacked vertically, input split to match).
+    """
+    w = np.asarray(w)
+    height = _check_split(w.shape[0], n, "row split")
+    return w[s * height:(s + 1) * height, :]
+
+
+def x_block(x, n: int, s: int) -> np.ndarray:
+    """X_s: the input columns matching row block s of W ([TP-topic] "Row-Wise Parallelism")."""
+    x = np.asarray(x)
+    width = _check_split(x.shape[1], n, "input split")
+    return x[:, s * width:(s + 1) * width]
+
+
+def concat_cols(blocks) -> np.ndarray:
+    """Place column-shard outputs side by side, block 0 first.
+
+    The combine step of the column split ([TP-topic] "Column-Wise Parallelism",
+    all-gather / concatenation; [AI-gloss] "Check your understanding": outputs
+    at different coordinates are concatenated).
+    """
+    return np.concatenate([widen(b) for b in blocks], axis=1)
+
+
+def reduce_sum(partials) -> np.ndarray:
+    """Sum partial outputs that share coordinates, in ascending shard order, float64.
+
+    The combine step of the row split ([TP-topic] "Row-Wise Parallelism",
+    Y = sum_i Y_i via all-reduce; [AI-gloss] "Check your understanding":
+    contributions to the same coordinates are added).
+    """
+    partials = list(partials)
+    if not partials:
+        raise ValueError("reduce_sum needs at least one partial")
+    total = widen(partials[0]).copy()
+    for p in partials[1:]:
+        total = total + widen(p)
+    return total
+
+
+def gelu(x) -> np.ndarray:
+    """Exact GeLU: x * Phi(x) = 0.5 * x * (1 + erf(x / sqrt(2))), float64.
+
+    The pages name only an activation applied to each shard on its own
+    ([TP-topic] "Megatron-LM Tensor Parallelism", MLP splitting); the exact
+    erf form of GeLU is the reading taken here.
+    """
+    x = widen(x)
+    return 0.5 * x * (1.0 + _erf(x / np.sqrt(2.0)))
+
+
+def apply_act(y, act: str) -> np.ndarray:
+    if act == "none":
+        return widen(y)
+    if act == "gelu":
+        return gelu(y)
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def col_shard_outputs(x, w, n: int, act: str = "none", s0: int = 0, ns: int | None = None):
+    """Y_s = act(X W_s) for s in s0 .. s0+ns-1 ([TP-topic] "Column-Wise Parallelism").
+
+    X is replicated to every shard; each shard's block of output columns is
+    computed independently (the activation, being elementwise, needs no exchange).
+    """
+    ns = n - s0 if ns is None else ns
+    return [apply_act(matmul(x, col_block(w, n, s)), act) for s in range(s0, s0 + ns)]
+
+
+def col_linear(x, w, n: int, act: str = "none", s0: int = 0, ns: int | None = None) -> np.ndarray:
+    """Column-parallel linear: concatenation of the column-shard outputs."""
+    return concat_cols(col_shard_outputs(x, w, n, act, s0, ns))
+
+
+def row_partials(x, w, n: int, s0: int = 0, ns: int | None = None):
+    """P_s = X_s W_s for s in s0 .. s0+ns-1 ([TP-topic] "Row-Wise Parallelism")."""
+    ns = n - s0 if ns is None else ns
+    return [matmul(x_block(x, n, s), row_block(w, n, s)) for s in range(s0, s0 + ns)]
+
+
+def row_linear(x, w, n: int, s0: int = 0, ns: int | None = None) -> np.ndarray:
+    """Row-parallel linear: sum of the partials."""
+    return reduce_sum(row_partials(x, w, n, s0, ns))
+
+
+def mlp_shard_partials(x, w1, w2, n: int, act: str = "gelu", s0: int = 0, ns: int | None = None):
+    """Per-shard outputs of the Megatron MLP pair ([TP-topic] "Megatron-LM Tensor Parallelism").
+
+    Shard s applies the column block s of W1, the activation on its own
+    columns, then the row block s of W2; both blocks cover the same slice
+    s*F/N .. (s+1)*F/N of the intermediate width, which is why the
+    intermediate H never leaves its shard ([TP-topic] "Row-Wise Parallelism":
+    the input is already split by the preceding column-wise layer).
+    H stays float64 here.
+    """
+    ns = n - s0 if ns is None else ns
+    out = []
+    for s in range(s0, s0 + ns):
+        h_s = apply_act(matmul(x, col_block(w1, n, s)), act)
+        out.append(matmul(h_s, row_block(w2, n, s)))
+    return out
+
+
+def mlp(x, w1, w2, n: int, act: str = "gelu", s0: int = 0, ns: int | None = None) -> np.ndarray:
+    """Y = sum_s act(X W1_s) W2_s, the single sum closing the MLP pair."""
+    return reduce_sum(mlp_shard_partials(x, w1, w2, n, act, s0, ns))
