@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Benchmark of the tensor-parallel sharded linear layer on one MI355X.
+
+One step is one pass of the whole sharded MLP hot path over one batch of
+seeded synthetic input already resident in HBM: the column-parallel product
+with the GeLU epilogue (the intermediate stays partitioned by shard), the
+row-parallel products into fp32 partials, and the partial-sum reduce, for all
+N shards of the Megatron MLP block X [2048, 4096], W1 [4096, 16384],
+W2 [16384, 4096], N = 8. The three calls are exactly the ones tp_mlp issues
+for this shape; calling them one by one lets HIP events on the launch stream
+time each kernel inside the timed region.
+
+Prints one JSON line (rank 0). Extra workloads (the attention projections, one
+shard of a GPT-3-width MLP, and the decode-shaped MLP reported in HBM GB/s)
+are measured too and listed under "secondary"; --workload picks one.
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["gemm_mfma.hip", "gemm_skinny.hip", "combine.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tensor_sharded_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if stale/absent."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("workloads", {}).get(workload, {}).get(kernel)
+
+
+# ----------------------------------------------------------------------------- workloads
+
+
+def make_inputs(name, torch, dev):
+    """Seeded synthetic inputs of one workload, uploaded as bf16 bit patterns."""
+    from synthetic import WORKLOADS, normal_bf16
+
+    wl = WORKLOADS[name]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t = {"wl": wl}
+    if name in ("megatron_mlp", "gpt3_mlp_shard"):
+        width = wl.F // wl.N
+        t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
+        if wl.ns == wl.N:
+            t["w1"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
+            t["w2"] = up(normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)[0])
+        else:  # one GPU's share: only the executed shard's blocks are stored
+            t["w1"] = up(normal_bf16((wl.ns, wl.d, width), 0.02, wl.wid, 1)[0])
+            t["w2"] = up(normal_bf16((wl.ns, width, wl.d), 0.02, wl.wid, 2)[0])
+    elif name == "attn_proj":
+        t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
+        t["wqkv"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
+        t["wo"] = up(normal_bf16((wl.d, wl.out), 0.02, wl.wid, 2)[0])
+        t["a"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 3)[0])
+    elif name == "decode_mlp":
+        width = wl.F // wl.N
+        t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
+        # two weight sets used alternately, so no step finds the previous step's weights in cache
+        t["w1s"] = [up(normal_bf16((wl.N, wl.d, width), 0.02, wl.wid + 100 * r, 1)[0]) for r in range(2)]
+        t["w2s"] = [up(normal_bf16((wl.N, width, wl.d), 0.02, wl.wid + 100 * r, 2)[0]) for r in range(2)]
+    else:
+        raise ValueError(name)
+    return t
+
+
+def plan(name, t, torch, tp):
+    """Returns (kernels, step) where step(i, rec) issues one step and calls rec() between kernels."""
+    wl = t["wl"]
+    dev = t["x"].device
+    flop = lambda m, k, n: 2.0 * m * k * n  # noqa: E731
+    if name in ("megatron_mlp", "gpt3_mlp_shard"):
+        width = wl.F // wl.N
+        h = torch.empty((wl.M, wl.ns * width), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((wl.M, wl.d), dtype=torch.float32, device=dev)
+        p = torch.empty((wl.ns, wl.M, wl.d), dtype=torch.float32, device=dev) if wl.ns > 1 else None
+        kernels = [
+            {"name": "col_gemm_gelu", "flop": flop(wl.M, wl.d, wl.ns * width), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.d + wl.d * wl.ns * width + wl.M * wl.ns * width)},
+            {"name": "row_gemm_partials", "flop": flop(wl.M, wl.ns * width, wl.d), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.ns * width + wl.ns * width * wl.d) + 4.0 * wl.ns * wl.M * wl.d},
+        ]
+        if wl.ns > 1:
+            kernels.append({"name": "reduce_partials", "flop": 0.0, "bound": "hbm",
+                            "bytes": 4.0 * (wl.ns + 1) * wl.M * wl.d})
+
+        def step(i, rec):
+            tp.col_linear(t["x"], t["w1"], wl.N, 0, wl.ns, act="gelu", out=h)
+            rec()
+            if wl.ns > 1:
+                tp.row_linear(h, t["w2"] if t["w2"].dim() == 3 else t["w2"][: wl.ns * width], wl.ns, out=p)
+                rec()
+                tp.reduce_partials(p, "rows", out=y)
+            else:
+                tp.row_linear(h, t["w2"], 1, out=y.view(1, wl.M, wl.d))
+            rec()
+
+        return kernels, step
+    if name == "attn_proj":
+        width = wl.F // wl.N
+        qkv = torch.empty((wl.M, wl.F), dtype=torch.bfloat16, device=dev)
+        p = torch.empty((wl.N, wl.M, wl.out), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.M, wl.out), dtype=torch.float32, device=dev)
+        kb = wl.d // wl.N
+        kernels = [
+            {"name": "qkv_col_gemm", "flop": flop(wl.M, wl.d, wl.F), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.d + wl.d * wl.F + wl.M * wl.F)},
+            {"name": "wo_row_gemm_partials", "flop": flop(wl.M, wl.d, wl.out), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.d + wl.d * wl.out) + 4.0 * wl.N * wl.M * wl.out},
+            {"name": "reduce_partials", "flop": 0.0, "bound": "hbm", "bytes": 4.0 * (wl.N + 1) * wl.M * wl.out},
+        ]
+        del width, kb
+
+        def step(i, rec):
+            tp.col_linear(t["x"], t["wqkv"], wl.N, out=qkv)
+            rec()
+            tp.row_linear(t["a"], t["wo"], wl.N, out=p)
+            rec()
+            tp.reduce_partials(p, "rows", out=y)
+            rec()
+
+        return kernels, step
+    if name == "decode_mlp":
+        width = wl.F // wl.N
+        y = torch.empty((wl.M, wl.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(tp.mlp_workspace_bytes(t["x"], t["w1s"][0], t["w2s"][0], wl.N), dtype=torch.uint8,
+                         device=dev)
+        wbytes = 2.0 * (wl.d * wl.F + wl.F * wl.d)
+        kernels = [{"name": "decode_mlp", "flop": 2 * flop(wl.M, wl.d, wl.F), "bound": "hbm",
+                    "bytes": wbytes + 2.0 * wl.M * wl.d + 4.0 * wl.M * wl.d}]
+
+        def step(i, rec):
+            r = i % 2
+            tp.mlp(t["x"], t["w1s"][r], t["w2s"][r], wl.N, out=y, workspace=ws)
+            rec()
+
+        return kernels, step
+    raise ValueError(name)
+
+
+def time_workload(name, steps, warmup, torch, tp):
+    dev = torch.device("cuda:0")
+    t = make_inputs(name, torch, dev)
+    kernels, step = plan(name, t, torch, tp)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        step(i, lambda: None)
+    torch.cuda.synchronize()
+    nk = len(kernels)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        marks = ev[i]
+        marks[0].record(stream)
+        k = [1]
+
+        def rec(marks=marks, k=k):
+            marks[k[0]].record(stream)
+            k[0] += 1
+
+        step(i, rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(nk)] for i in range(steps)])
+    step_ms = np.array([ev[i][0].elapsed_time(ev[i][nk]) for i in range(steps)])
+    res = {"workload": name, "steps": steps, "ms_per_step": float(step_ms.mean()),
+           "ms_per_step_min": float(step_ms.min()), "wall_s": wall, "kernels": []}
+    total_flop = sum(k["flop"] for k in kernels)
+    for j, k in enumerate(kernels):
+        ms = float(per_kernel[:, j].mean())
+        entry = {"name": k["name"], "ms": ms, "ms_min": float(per_kernel[:, j].min()), "bound": k["bound"]}
+        if k["flop"]:
+            entry["tflops"] = k["flop"] / (ms * 1e-3) / 1e12
+            entry["frac_mfma_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
+        entry["alg_gbs"] = k["bytes"] / (ms * 1e-3) / 1e9
+        entry["frac_hbm_peak"] = entry["alg_gbs"] / PEAK_HBM_GBS
+        res["kernels"].append(entry)
+    res["tflops"] = total_flop / (res["ms_per_step"] * 1e-3) / 1e12
+    if name == "decode_mlp":
+        res["alg_bytes"] = kernels[0]["bytes"]
+        res["gbs"] = kernels[0]["bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
+    res["_kernels_def"] = kernels
+    return res
+
+
+def roofline_for(res):
+    """The dominant kernel of a workload against its bound."""
+    ks = res["kernels"]
+    j = int(np.argmax([k["ms"] for k in ks]))
+    k, kd = ks[j], res["_kernels_def"][j]
+    traffic = measured_traffic(res["workload"], k["name"])
+    if kd["bound"] == "mfma":
+        achieved = kd["flop"] / (k["ms"] * 1e-3) / 1e12
+        return {"kernel": k["name"], "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "alg_per_launch": kd["flop"], "ms_per_launch": k["ms"]}
+    achieved = kd["bytes"] / (k["ms"] * 1e-3) / 1e9
+    return {"kernel": k["name"], "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "alg_per_launch": kd["bytes"],
+            "ms_per_launch": k["ms"]}
+
+
+def cpu_baseline(seconds_target: float = 15.0):
+    """The float64 oracle timed on the host cores on a bounded sample of the Megatron MLP workload."""
+    import oracle
+    from synthetic import WORKLOADS, normal_bf16
+
+    wl = WORKLOADS["megatron_mlp"]
+    _, x = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)
+    _, w1 = normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)
+    _, w2 = normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    rows = 64
+    t0 = time.perf_counter()
+    oracle.mlp(x[:rows], w1, w2, wl.N, "gelu")
+    dt = time.perf_counter() - t0
+    # grow the sample towards the time target (bounded by the workload's rows)
+    rows = int(min(wl.M, max(64, rows * seconds_target / max(dt, 1e-3) * 0.8)))
+    t0 = time.perf_counter()
+    oracle.mlp(x[:rows], w1, w2, wl.N, "gelu")
+    dt = time.perf_counter() - t0
+    flops = 2 * 2.0 * rows * wl.d * wl.F
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {wl.M} token rows of the megatron_mlp workload, all {wl.N} shards, "
+                      f"float64 numpy oracle, {dt:.1f} s",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def copy_calibration(torch, gib: float = 1.0):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the sharded layer runs all N logical shards on a single "
+              "MI355X; no multi-GPU figure is produced. Use --gpus 1.", file=sys.stderr)
+        sys.exit(1)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    import tensor_sharded_linear_amd as tp
+
+    tp.library()  # fails loudly if the HIP library is missing
+    main_name = "megatron_mlp" if args.workload in ("all", "megatron_mlp") else args.workload
+    names = [main_name] if args.workload != "all" else ["megatron_mlp", "attn_proj", "gpt3_mlp_shard",
+                                                        "decode_mlp"]
+    results = {}
+    for name in names:
+        steps = args.steps if name in ("megatron_mlp", "decode_mlp") else max(3, args.steps // 5)
+        print(f"[bench] {name}: warmup {args.warmup}, steps {steps}", file=sys.stderr, flush=True)
+        results[name] = time_workload(name, steps, args.warmup, torch, tp)
+        torch.cuda.empty_cache()
+        print(f"[bench] {name}: {results[name]['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+
+    main = results[main_name]
+    from synthetic import WORKLOADS
+
+    wl = WORKLOADS[main_name]
+    if main_name == "decode_mlp":
+        metric, unit, value = "decode-shape HBM GB/s", "GB/s", main["gbs"]
+    else:
+        metric, unit, value = "sharded-linear TFLOP/s", "TFLOP/s", main["tflops"]
+    line = {
+        "metric": metric,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": main["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": main["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, rounded to bf16)",
+        "config": {"workload": main_name, "M": wl.M, "d": wl.d, "F": wl.F, "N": wl.N, "shards_run": wl.ns,
+                   "parallelism": f"tp{wl.N} shards executed on 1 GPU"},
+        "frac_of_bf16_peak": (main["tflops"] / PEAK_BF16_TFLOPS) if main_name != "decode_mlp" else None,
+        "roofline": roofline_for(main),
+        "kernels": main["kernels"],
+    }
+    secondary = []
+    for name in names:
+        if name == main_name:
+            continue
+        r = results[name]
+        entry = {"workload": name, "ms_per_step": r["ms_per_step"], "kernels": r["kernels"],
+                 "roofline": roofline_for(r)}
+        if name == "decode_mlp":
+            entry.update({"metric": "decode-shape HBM GB/s", "value": r["gbs"], "unit": "GB/s",
+                          "frac_of_hbm_peak": r["gbs"] / PEAK_HBM_GBS})
+        else:
+            entry.update({"metric": "sharded-linear TFLOP/s", "value": r["tflops"], "unit": "TFLOP/s",
+                          "frac_of_bf16_peak": r["tflops"] / PEAK_BF16_TFLOPS})
+        secondary.append(entry)
+    if secondary:
+        line["secondary"] = secondary
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on host cores)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

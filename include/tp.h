@@ -1,0 +1,185 @@
+/*
+ * tp.h - tensor-parallel sharded linear layer Y = X W on one MI355X (gfx950).
+ *
+ * The operation follows these web pages on tensor parallelism:
+ *   [TP-topic]  "Tensor Parallelism" topic page, chipfoundryservices.com
+ *   [AI-gloss]  "Tensor Parallelism" entry, AI Glossary, aiforbusinessandlife.com
+ *   [DLwPT]     "Tensor parallelism" concept page, Deep Learning with PyTorch 2e
+ *
+ * A weight W of logical shape [K, Nout] (rows = input features, columns =
+ * output features, Y = X W) is split over N logical shards, either by output
+ * columns (W = [W_0, ..., W_{N-1}], [TP-topic] "Column-Wise Parallelism") or
+ * by rows, i.e. the contracted dimension (W = [W_0; ...; W_{N-1}] with X split
+ * to match, [TP-topic] "Row-Wise Parallelism"). Shard s always owns the s-th
+ * contiguous block; N must divide the split dimension. All N shards (or a
+ * range of them) run on the one GPU, so the pages' all-gather becomes a
+ * concatenation in device memory and their all-reduce becomes an fp32 sum of
+ * partials in ascending shard order.
+ *
+ * Conventions shared by every entry point
+ *   Memory      Every tp_matrix points to device memory owned by the caller.
+ *               The library allocates and frees nothing and keeps no mutable
+ *               global state; descriptors are read before the call returns.
+ *   Streams     Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *               stream) and the call returns without waiting. Inputs must
+ *               stay alive and unchanged until the stream has passed the work.
+ *   Errors      Every argument is checked on the host before any HIP call; on
+ *               failure the call returns the status and enqueues nothing. A
+ *               failed launch returns TP_ERR_HIP. No C++ exception crosses
+ *               this interface.
+ *   Dtypes      X and W share one dtype. TP_BF16 runs on the bf16 matrix cores
+ *               with fp32 accumulation; TP_F32 runs an fp32 FMA path (exact on
+ *               integer-valued inputs whose partial sums stay below 2^24).
+ *               Partials and sums are fp32. bf16 outputs are rounded to
+ *               nearest-even from the fp32 result.
+ *   Layout      Row-major. `ld` is the distance in elements between rows.
+ *               Leading dimensions or pointers that are not 16-byte aligned,
+ *               or widths that are not multiples of 8, select a slower
+ *               element-guarded kernel; they are not an error.
+ *   Aliasing    An output may not overlap any input (TP_ERR_ALIAS).
+ *   Empty       A zero-sized output is a successful no-op. K = 0 gives act(0).
+ */
+#ifndef TP_H
+#define TP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tp_status {
+  TP_OK = 0,
+  TP_ERR_NULL = 1,         /* a descriptor, data pointer or out-parameter is NULL */
+  TP_ERR_DTYPE = 2,        /* unsupported dtype, or X and W dtypes differ, or P not fp32 */
+  TP_ERR_SHAPE = 3,        /* negative size, or shapes that do not chain (X.cols != W.rows, ...) */
+  TP_ERR_INDIVISIBLE = 4,  /* N < 1 or N does not divide the split dimension */
+  TP_ERR_SHARD_RANGE = 5,  /* s0 < 0, ns < 1 or s0 + ns > N */
+  TP_ERR_STRIDE = 6,       /* ld shorter than a row, or shard blocks that overlap */
+  TP_ERR_ALIAS = 7,        /* an output overlaps an input */
+  TP_ERR_WORKSPACE = 8,    /* workspace missing or smaller than required */
+  TP_ERR_HIP = 9,          /* a kernel launch failed */
+  TP_ERR_TOO_LARGE = 10    /* a size exceeds the 32-bit tile/launch limits of the kernels */
+} tp_status;
+
+typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Which dimension of W is split: its output columns, or its rows (the contracted dimension). */
+typedef enum tp_axis { TP_SPLIT_COLS = 0, TP_SPLIT_ROWS = 1 } tp_axis;
+
+typedef enum tp_act { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_act;
+
+/*
+ * A row-major matrix in device memory, possibly stored as shard blocks.
+ *   ptr           element [0][0] (of block 0 when shard_stride > 0)
+ *   dtype         tp_dtype
+ *   rows, cols    the LOGICAL shape, as defined by each entry point
+ *   ld            elements between consecutive rows (of one block when shard_stride > 0)
+ *   shard_stride  0: the blocks are slices of one row-major matrix;
+ *                 > 0: shard-major storage, block j starts shard_stride
+ *                 elements after block j-1 (each block has its own rows with
+ *                 row stride ld); blocks may not overlap.
+ */
+typedef struct tp_matrix {
+  void* ptr;
+  int32_t dtype;
+  int32_t reserved; /* padding, ignored */
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;
+  int64_t shard_stride;
+} tp_matrix;
+
+/*
+ * Column-parallel linear ([TP-topic] "Column-Wise Parallelism"; [AI-gloss]
+ * "Worked example", column split). For s = s0 .. s0+ns-1, shard s computes
+ *     Y_j = act(X W_s),  j = s - s0,
+ * where W_s = W[:, s*Nout/N : (s+1)*Nout/N] and the activation is elementwise
+ * on the fp32 result ([TP-topic] "Megatron-LM Tensor Parallelism": applied on
+ * each shard without exchange; TP_ACT_GELU = x * Phi(x) with the exact erf).
+ *   X  [M, K], shard_stride 0 (the same X reaches every shard).
+ *   W  logical [K, Nout], N | Nout. shard_stride 0: W_s is the column slice
+ *      above (ld >= Nout); > 0: W_s is the [K, Nout/N] block at
+ *      ptr + s*shard_stride with row stride ld (ld >= Nout/N).
+ *   Y  logical [M, ns*Nout/N], dtype TP_F32 or TP_BF16. shard_stride 0: Y_j is
+ *      written at columns j*Nout/N (the concatenation, [TP-topic]
+ *      "Column-Wise Parallelism": output combination); > 0: Y_j is the
+ *      [M, Nout/N] block at ptr + j*shard_stride (outputs left partitioned,
+ *      [AI-gloss] "Worked example").
+ */
+tp_status tp_col_linear(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0, int32_t ns,
+                        int32_t act, const tp_matrix* Y, void* stream);
+
+/*
+ * Row-parallel linear, partial products only ([TP-topic] "Row-Wise
+ * Parallelism"; [AI-gloss] "Worked example", split along the input
+ * dimension). For s = s0 .. s0+ns-1, shard s computes the fp32 partial
+ *     P_j = X_s W_s,  j = s - s0,
+ * with X_s = X[:, s*K/N : (s+1)*K/N] and W_s = W[s*K/N : (s+1)*K/N, :].
+ *   X  logical [M, K], N | K. shard_stride 0: X_s is the column slice; > 0:
+ *      X_s is the [M, K/N] block at ptr + s*shard_stride (e.g. the
+ *      partitioned output of a column-parallel layer).
+ *   W  logical [K, Nout]. shard_stride 0: W_s is the row slice; > 0: the
+ *      [K/N, Nout] block at ptr + s*shard_stride.
+ *   P  dtype TP_F32, rows = M, cols = Nout; P_j at ptr + j*shard_stride with
+ *      row stride ld. shard_stride may be 0 only when ns = 1.
+ * Combine the partials with tp_reduce_partials(axis = TP_SPLIT_ROWS).
+ */
+tp_status tp_row_linear(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0, int32_t ns,
+                        const tp_matrix* P, void* stream);
+
+/*
+ * Combine n shard outputs ([AI-gloss] "Check your understanding": outputs
+ * for the same coordinates are added, outputs for different coordinates are
+ * concatenated; [TP-topic] "Tensor Parallelism Fundamentals").
+ *   P     n blocks of [rows, cols] at ptr + j*shard_stride, row stride ld,
+ *         dtype TP_F32 (axis ROWS) or TP_F32 / TP_BF16 (axis COLS).
+ *   axis  TP_SPLIT_ROWS: the contracted dimension was split, so
+ *           Y = P_0 + P_1 + ... + P_{n-1}, fp32, in ascending j
+ *         (the single-GPU form of the all-reduce);
+ *         TP_SPLIT_COLS: the output columns were split, so
+ *           Y = [P_0 | P_1 | ... | P_{n-1}]  (Y.cols = n*cols; the all-gather).
+ *   Y     [rows, cols] (ROWS) or [rows, n*cols] (COLS), dtype TP_F32 or
+ *         TP_BF16 (ROWS: rounded from the fp32 sum; COLS: converted, exact
+ *         when P and Y share a dtype), Y.shard_stride must be 0.
+ */
+tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const tp_matrix* Y, void* stream);
+
+/*
+ * Megatron-style tensor-parallel MLP forward ([TP-topic] "Megatron-LM Tensor
+ * Parallelism": the first linear split by columns, the activation on each
+ * shard, the second linear split by rows, one sum at the end):
+ *     Y = sum_{s=s0}^{s0+ns-1} act(X W1_s) W2_s        (fp32, ascending s)
+ * with W1_s = W1[:, s*F/N : (s+1)*F/N] and W2_s = W2[s*F/N : (s+1)*F/N, :];
+ * the same slice of the intermediate width F indexes both, so the
+ * intermediate H_s = act(X W1_s) never leaves its shard. With bf16 inputs H_s
+ * is rounded to bf16 before the second product.
+ *   X   [M, d], shard_stride 0.       W1 logical [d, F], N | F.
+ *   W2  logical [F, Dout].            shard_stride as in tp_col_linear (W1)
+ *                                     and tp_row_linear (W2).
+ *   Y   [M, Dout], TP_F32, shard_stride 0.
+ *   workspace, *workspace_bytes
+ *       device scratch for H and the partials (size depends on the shapes).
+ *       If workspace is NULL the required size is stored in *workspace_bytes
+ *       and TP_OK is returned with nothing enqueued (only shapes, dtypes and
+ *       strides are checked then; data pointers may be NULL); otherwise
+ *       *workspace_bytes must be at least that size. The workspace must not
+ *       overlap any operand. It may be reused once the stream has passed
+ *       the call.
+ */
+tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, int32_t N, int32_t s0,
+                 int32_t ns, int32_t act, void* workspace, size_t* workspace_bytes, const tp_matrix* Y,
+                 void* stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* tp_status_string(int32_t status);
+
+/* Version of this interface: (major << 16) | minor. */
+int32_t tp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_H */

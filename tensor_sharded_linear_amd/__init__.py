@@ -1,0 +1,211 @@
+"""Tensor-parallel sharded linear layer Y = X W on one MI355X (gfx950).
+
+Thin torch binding over the C interface of libtp_amd.so (include/tp.h):
+it reads data pointers, shapes and strides of torch tensors, passes the
+current HIP stream, and calls the library. Every step of the computation
+runs in the library's HIP kernels; this module computes nothing itself.
+
+Shard layouts accepted for weights and inputs:
+  * 2-D tensors: the logical full matrix; shard s is its s-th contiguous block
+    of columns (column split) or rows (row split);
+  * 3-D tensors [N, r, c]: shard-major storage, block s = t[s].
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (TP_ACT_GELU, TP_ACT_NONE, TP_BF16, TP_F32, TP_SPLIT_COLS, TP_SPLIT_ROWS, TpError,
+                   TpMatrix, status_string)
+
+__all__ = [
+    "col_linear",
+    "row_linear",
+    "reduce_partials",
+    "mlp",
+    "mlp_workspace_bytes",
+    "TpError",
+    "library",
+    "version",
+]
+
+_ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU}
+_AXES = {"rows": TP_SPLIT_ROWS, "cols": TP_SPLIT_COLS}
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    return _lib.load()
+
+
+def version() -> int:
+    return int(library().tp_version())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TP_F32
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _require_gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live in GPU memory")
+        if t.dim() >= 1 and t.numel() > 0 and t.stride(-1) != 1:
+            raise ValueError("the last dimension must be contiguous (stride 1)")
+
+
+def _full(t: torch.Tensor) -> TpMatrix:
+    """A 2-D tensor as one row-major matrix."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    return _lib.matrix(t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1], max(t.stride(0), t.shape[1]), 0)
+
+
+def _blocks(t: torch.Tensor, rows: int, cols: int) -> TpMatrix:
+    """A 2-D logical matrix, or a 3-D shard-major stack whose logical shape is (rows, cols)."""
+    if t.dim() == 2:
+        return _full(t)
+    if t.dim() != 3:
+        raise ValueError("expected a 2-D matrix or a 3-D shard-major stack")
+    ld = max(t.stride(1), t.shape[2])
+    stride = t.stride(0) if t.shape[0] > 1 else max(1, (t.shape[1] - 1) * ld + t.shape[2])
+    return _lib.matrix(t.data_ptr(), _dtype_code(t), rows, cols, ld, stride)
+
+
+def _check_stack(t: torch.Tensor, s0: int, ns: int) -> None:
+    """A shard-major stack [blocks, r, c] must hold block s for every executed shard s (block s = t[s])."""
+    if t.dim() == 3 and t.shape[0] < s0 + ns:
+        raise ValueError(f"shard-major stack holds {t.shape[0]} blocks, shards up to {s0 + ns - 1} are executed")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def col_linear(x: torch.Tensor, w: torch.Tensor, n: int, s0: int = 0, ns: int | None = None, act: str = "none",
+               out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
+               partitioned: bool = False) -> torch.Tensor:
+    """Column-parallel linear: Y_j = act(X W_{s0+j}) for the executed shards.
+
+    w: [K, Nout] (shard s = columns s*Nout/n ...) or shard-major [n, K, Nout/n].
+    Returns Y [M, ns*Nout/n] (concatenated), or [ns, M, Nout/n] if partitioned.
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(x, w)
+    k = x.shape[1]
+    _check_stack(w, s0, ns)
+    nout = w.shape[1] if w.dim() == 2 else n * w.shape[2]
+    width = nout // n if n > 0 else 0
+    od = out_dtype or (out.dtype if out is not None else x.dtype)
+    if out is None:
+        shape = (ns, x.shape[0], width) if partitioned else (x.shape[0], ns * width)
+        out = torch.empty(shape, dtype=od, device=x.device)
+    _require_gpu(out)
+    if out.dim() == 3:
+        ym = _lib.matrix(out.data_ptr(), _dtype_code(out), out.shape[1], ns * width,
+                         max(out.stride(1), out.shape[2]),
+                         out.stride(0) if out.shape[0] > 1 else max(1, (out.shape[1] - 1) * out.stride(1) + width))
+    else:
+        ym = _full(out)
+    xm = _full(x)
+    wm = _blocks(w, k, nout)
+    st = library().tp_col_linear(ctypes.byref(xm), ctypes.byref(wm), n, s0, ns, _ACTS[act], ctypes.byref(ym),
+                                 ctypes.c_void_p(_stream(x)))
+    _lib.check(st, "tp_col_linear")
+    return out
+
+
+def row_linear(x: torch.Tensor, w: torch.Tensor, n: int, s0: int = 0, ns: int | None = None,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-parallel partial products P_j = X_{s0+j} W_{s0+j} (fp32), returned as [ns, M, Nout].
+
+    x: [M, K] (shard s = columns s*K/n ...) or shard-major [n, M, K/n].
+    w: [K, Nout] (shard s = rows s*K/n ...) or shard-major [n, K/n, Nout].
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(x, w)
+    _check_stack(x, s0, ns)
+    _check_stack(w, s0, ns)
+    m = x.shape[0] if x.dim() == 2 else x.shape[1]
+    k = x.shape[1] if x.dim() == 2 else n * x.shape[2]
+    nout = w.shape[1] if w.dim() == 2 else w.shape[2]
+    if out is None:
+        out = torch.empty((ns, m, nout), dtype=torch.float32, device=x.device)
+    _require_gpu(out)
+    xm = _blocks(x, m, k)
+    wm = _blocks(w, k, nout)
+    pm = _lib.matrix(out.data_ptr(), _dtype_code(out), m, nout, max(out.stride(1), nout),
+                     out.stride(0) if out.shape[0] > 1 else 0)
+    st = library().tp_row_linear(ctypes.byref(xm), ctypes.byref(wm), n, s0, ns, ctypes.byref(pm),
+                                 ctypes.c_void_p(_stream(x)))
+    _lib.check(st, "tp_row_linear")
+    return out
+
+
+def reduce_partials(p: torch.Tensor, axis: str = "rows", out: torch.Tensor | None = None,
+                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Combine shard outputs p [n, R, C]: sum (axis="rows") or concatenation (axis="cols")."""
+    _require_gpu(p)
+    n, r, c = p.shape
+    if out is None:
+        out = torch.empty((r, c if axis == "rows" else n * c), dtype=out_dtype, device=p.device)
+    _require_gpu(out)
+    pm = _lib.matrix(p.data_ptr(), _dtype_code(p), r, c, max(p.stride(1), c), p.stride(0) if n > 1 else 0)
+    ym = _full(out)
+    st = library().tp_reduce_partials(ctypes.byref(pm), n, _AXES[axis], ctypes.byref(ym),
+                                      ctypes.c_void_p(_stream(p)))
+    _lib.check(st, "tp_reduce_partials")
+    return out
+
+
+def _mlp_mats(x, w1, w2, n):
+    d = x.shape[1]
+    f = w1.shape[1] if w1.dim() == 2 else n * w1.shape[2]
+    dout = w2.shape[1] if w2.dim() == 2 else w2.shape[2]
+    return _full(x), _blocks(w1, d, f), _blocks(w2, f, dout), dout
+
+
+def mlp_workspace_bytes(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, n: int, s0: int = 0,
+                        ns: int | None = None, act: str = "gelu") -> int:
+    """Device scratch that mlp() needs for these operands (query of the library)."""
+    ns = n - s0 if ns is None else ns
+    _check_stack(w1, s0, ns)
+    _check_stack(w2, s0, ns)
+    xm, w1m, w2m, dout = _mlp_mats(x, w1, w2, n)
+    ym = _lib.matrix(0, TP_F32, x.shape[0], dout, dout, 0)
+    size = ctypes.c_size_t(0)
+    st = library().tp_mlp(ctypes.byref(xm), ctypes.byref(w1m), ctypes.byref(w2m), n, s0, ns, _ACTS[act], None,
+                          ctypes.byref(size), ctypes.byref(ym), None)
+    _lib.check(st, "tp_mlp(workspace query)")
+    return int(size.value)
+
+
+def mlp(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, n: int, s0: int = 0, ns: int | None = None,
+        act: str = "gelu", out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Megatron MLP pair: Y = sum_s act(X W1_s) W2_s over the executed shards, fp32 [M, Dout].
+
+    w1: [d, F] or shard-major [n, d, F/n]; w2: [F, Dout] or shard-major [n, F/n, Dout].
+    workspace: optional uint8 device tensor of at least mlp_workspace_bytes(...) bytes.
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(x, w1, w2)
+    xm, w1m, w2m, dout = _mlp_mats(x, w1, w2, n)
+    if out is None:
+        out = torch.empty((x.shape[0], dout), dtype=torch.float32, device=x.device)
+    _require_gpu(out)
+    need = mlp_workspace_bytes(x, w1, w2, n, s0, ns, act)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ym = _full(out)
+    size = ctypes.c_size_t(workspace.numel())
+    st = library().tp_mlp(ctypes.byref(xm), ctypes.byref(w1m), ctypes.byref(w2m), n, s0, ns, _ACTS[act],
+                          ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(size), ctypes.byref(ym),
+                          ctypes.c_void_p(_stream(x)))
+    _lib.check(st, "tp_mlp")
+    return out

@@ -1,0 +1,112 @@
+// Combining shard outputs on one GPU.
+//
+// Sum (the local form of the all-reduce): Y = P_0 + P_1 + ... + P_{n-1} in
+// fp32, added in ascending shard order so that every run gives the same bits.
+// Concatenation (the local form of the all-gather): Y = [P_0 | ... | P_{n-1}].
+// The rule for choosing between them is the one of the "Tensor Parallelism"
+// entry of the AI Glossary (aiforbusinessandlife.com), "Check your
+// understanding": partial results for the same output coordinates are added,
+// results for different coordinates are concatenated; the collectives are
+// those of the "Tensor Parallelism" topic page (chipfoundryservices.com),
+// "Tensor Parallelism Fundamentals".
+//
+// Both are bound by HBM traffic: every lane streams 16-byte vectors.
+#include "tp_internal.h"
+
+namespace tp {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t grid_threads() { return (int64_t)gridDim.x * blockDim.x; }
+__device__ __forceinline__ int64_t thread_index() { return (int64_t)blockIdx.x * blockDim.x + threadIdx.x; }
+
+template <bool YBF16>
+__global__ __launch_bounds__(256) void sum_vec4_kernel(CombineDesc d) {
+  const int64_t c4 = d.cols >> 2;
+  const int64_t total = d.rows * c4;
+  const float* P = static_cast<const float*>(d.P);
+  for (int64_t i = thread_index(); i < total; i += grid_threads()) {
+    const int64_t r = i / c4, c = (i - r * c4) << 2;
+    const float* src = P + r * d.ldp + c;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+    for (int j = 1; j < d.n; ++j) acc += *reinterpret_cast<const f32x4*>(src + (int64_t)j * d.sP);
+    if (YBF16) {
+      bf16x4 h;
+      h[0] = (__bf16)acc[0]; h[1] = (__bf16)acc[1]; h[2] = (__bf16)acc[2]; h[3] = (__bf16)acc[3];
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(d.Y) + r * d.ldy + c) = h;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(d.Y) + r * d.ldy + c) = acc;
+    }
+  }
+}
+
+template <bool YBF16>
+__global__ __launch_bounds__(256) void sum_scalar_kernel(CombineDesc d) {
+  const int64_t total = d.rows * d.cols;
+  const float* P = static_cast<const float*>(d.P);
+  for (int64_t i = thread_index(); i < total; i += grid_threads()) {
+    const int64_t r = i / d.cols, c = i - r * d.cols;
+    const float* src = P + r * d.ldp + c;
+    float acc = src[0];
+    for (int j = 1; j < d.n; ++j) acc += src[(int64_t)j * d.sP];
+    if (YBF16) static_cast<__bf16*>(d.Y)[r * d.ldy + c] = (__bf16)acc;
+    else static_cast<float*>(d.Y)[r * d.ldy + c] = acc;
+  }
+}
+
+template <bool PBF16, bool YBF16>
+__global__ __launch_bounds__(256) void concat_kernel(CombineDesc d) {
+  const int64_t per = d.rows * d.cols;
+  const int64_t total = per * d.n;
+  for (int64_t i = thread_index(); i < total; i += grid_threads()) {
+    const int64_t j = i / per, rem = i - j * per;
+    const int64_t r = rem / d.cols, c = rem - r * d.cols;
+    const int64_t src = j * d.sP + r * d.ldp + c;
+    const float v = PBF16 ? (float)static_cast<const __bf16*>(d.P)[src] : static_cast<const float*>(d.P)[src];
+    const int64_t dst = r * d.ldy + j * d.cols + c;
+    if (YBF16) static_cast<__bf16*>(d.Y)[dst] = (__bf16)v;
+    else static_cast<float*>(d.Y)[dst] = v;
+  }
+}
+
+dim3 grid_for(int64_t work) {
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 8192) blocks = 8192;  // 32 workgroups per CU, grid-stride beyond
+  if (blocks < 1) blocks = 1;
+  return dim3((unsigned)blocks);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineDesc& d, hipStream_t stream) {
+  if (d.rows <= 0 || d.cols <= 0 || d.n <= 0) return hipSuccess;
+  const dim3 block(256);
+  if (d.concat) {
+    const dim3 grid = grid_for(d.rows * d.cols * d.n);
+    if (d.p_bf16) {
+      if (d.y_bf16) concat_kernel<true, true><<<grid, block, 0, stream>>>(d);
+      else concat_kernel<true, false><<<grid, block, 0, stream>>>(d);
+    } else {
+      if (d.y_bf16) concat_kernel<false, true><<<grid, block, 0, stream>>>(d);
+      else concat_kernel<false, false><<<grid, block, 0, stream>>>(d);
+    }
+    return hipGetLastError();
+  }
+  const bool vec = (d.cols % 4 == 0) && (d.ldp % 4 == 0) && (d.sP % 4 == 0) && (d.ldy % 4 == 0) &&
+                   (reinterpret_cast<uintptr_t>(d.P) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(d.Y) % (d.y_bf16 ? 8 : 16) == 0);
+  if (vec) {
+    const dim3 grid = grid_for(d.rows * (d.cols / 4));
+    if (d.y_bf16) sum_vec4_kernel<true><<<grid, block, 0, stream>>>(d);
+    else sum_vec4_kernel<false><<<grid, block, 0, stream>>>(d);
+  } else {
+    const dim3 grid = grid_for(d.rows * d.cols);
+    if (d.y_bf16) sum_scalar_kernel<true><<<grid, block, 0, stream>>>(d);
+    else sum_scalar_kernel<false><<<grid, block, 0, stream>>>(d);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tp

@@ -1,0 +1,392 @@
+// Host side of the C interface in include/tp.h: argument checks (all before
+// any HIP call), shard views (pointer + stride arithmetic, no data movement),
+// kernel choice, workspace planning and launches on the caller's stream.
+//
+// The shard views follow the "Tensor Parallelism" topic page
+// (chipfoundryservices.com): "Column-Wise Parallelism" (W = [W_1, ..., W_N],
+// shard i computes X W_i) and "Row-Wise Parallelism" (W stacked by rows, X
+// split to match, partial products summed). Shard s owns the s-th contiguous
+// block of the split dimension; the split must be even.
+#include <cstring>
+
+#include "tp.h"
+#include "tp_internal.h"
+
+namespace {
+
+using tp::CombineDesc;
+using tp::GemmDesc;
+
+int64_t elt_size(int32_t dtype) { return dtype == TP_BF16 ? 2 : 4; }
+bool valid_dtype(int32_t dtype) { return dtype == TP_F32 || dtype == TP_BF16; }
+
+// Address range [lo, hi) touched by `nblocks` blocks of [brows, bcols] with row
+// stride ld and block stride `stride` (elements).
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+};
+
+Range range_of(const void* ptr, int32_t dtype, int64_t nblocks, int64_t stride, int64_t brows, int64_t bcols,
+               int64_t ld) {
+  Range r;
+  if (nblocks <= 0 || brows <= 0 || bcols <= 0) return r;
+  const int64_t elems = (nblocks - 1) * stride + (brows - 1) * ld + bcols;
+  r.lo = reinterpret_cast<uintptr_t>(ptr);
+  r.hi = r.lo + (uintptr_t)(elems * elt_size(dtype));
+  return r;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  if (a.hi <= a.lo || b.hi <= b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Sizes beyond these would overflow the kernels' 32-bit tile and grid arithmetic.
+constexpr int64_t kMaxDim = (1ll << 31) - 1;
+
+// Checks one matrix holding `nblocks` blocks of [brows, bcols]:
+//   shard_stride == 0 -> the blocks are slices of one matrix whose rows need
+//                        `row_len` elements (ld >= row_len);
+//   shard_stride  > 0 -> each block has row stride ld >= bcols and the blocks
+//                        must not overlap.
+tp_status check_matrix(const tp_matrix* m, int64_t nblocks, int64_t brows, int64_t bcols, int64_t row_len,
+                       bool need_ptr = true) {
+  if (!m) return TP_ERR_NULL;
+  if (!valid_dtype(m->dtype)) return TP_ERR_DTYPE;
+  if (m->rows < 0 || m->cols < 0) return TP_ERR_SHAPE;
+  if (m->rows > kMaxDim || m->cols > kMaxDim) return TP_ERR_TOO_LARGE;
+  if (m->ld < 0 || m->shard_stride < 0) return TP_ERR_STRIDE;
+  const bool empty = nblocks <= 0 || brows <= 0 || bcols <= 0;
+  if (m->shard_stride == 0) {
+    if (!empty && m->ld < row_len) return TP_ERR_STRIDE;
+  } else {
+    if (!empty && m->ld < bcols) return TP_ERR_STRIDE;
+    if (!empty && nblocks > 1 && m->shard_stride < (brows - 1) * m->ld + bcols) return TP_ERR_STRIDE;
+  }
+  if (need_ptr && !empty && !m->ptr) return TP_ERR_NULL;
+  return TP_OK;
+}
+
+tp_status hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
+
+// Runs one batched product with the best kernel the operands allow.
+hipError_t run_gemm(const GemmDesc& d, hipStream_t stream) {
+  if (d.M <= 0 || d.N <= 0 || d.batch <= 0) return hipSuccess;
+  if (d.in_bf16 && d.M <= tp::kSkinnyMaxRows && tp::gemm_skinny_supported(d))
+    return tp::launch_gemm_skinny(d, 1, nullptr, stream);
+  if (tp::gemm_mfma_supported(d)) return tp::launch_gemm_mfma(d, stream);
+  return tp::launch_gemm_generic(d, stream);
+}
+
+struct ColPlan {
+  GemmDesc g;
+  Range x, w, y;
+};
+
+// Column-parallel views: Y_j = act(X W_{s0+j}).
+tp_status plan_col(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0, int32_t ns, int32_t act,
+                   const tp_matrix* Y, ColPlan* out, bool need_ptr = true) {
+  if (!X || !W || !Y) return TP_ERR_NULL;
+  if (!valid_dtype(X->dtype) || !valid_dtype(W->dtype) || !valid_dtype(Y->dtype)) return TP_ERR_DTYPE;
+  if (X->dtype != W->dtype) return TP_ERR_DTYPE;
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU) return TP_ERR_SHAPE;
+  if (X->rows < 0 || X->cols < 0 || W->rows < 0 || W->cols < 0 || Y->rows < 0 || Y->cols < 0) return TP_ERR_SHAPE;
+  if (N < 1 || W->cols % N != 0) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int64_t M = X->rows, K = X->cols, width = W->cols / N;
+  if (W->rows != K) return TP_ERR_SHAPE;
+  if (Y->rows != M || Y->cols != (int64_t)ns * width) return TP_ERR_SHAPE;
+  if (X->shard_stride != 0) return TP_ERR_STRIDE;
+  tp_status st;
+  if ((st = check_matrix(X, 1, M, K, K, need_ptr)) != TP_OK) return st;
+  if ((st = check_matrix(W, ns, K, width, W->cols, need_ptr)) != TP_OK) return st;
+  if ((st = check_matrix(Y, ns, M, width, Y->cols, need_ptr)) != TP_OK) return st;
+
+  GemmDesc g;
+  std::memset(&g, 0, sizeof(g));
+  g.in_bf16 = X->dtype == TP_BF16;
+  g.out_kind = Y->dtype == TP_BF16 ? tp::OUT_BF16 : tp::OUT_F32;
+  g.act = act;
+  g.M = M;
+  g.K = K;
+  g.A = X->ptr;
+  g.lda = X->ld;
+  g.sA = 0;
+  const int64_t we = elt_size(W->dtype);
+  const char* wbase = static_cast<const char*>(W->ptr);
+  if (W->shard_stride == 0) wbase += (int64_t)s0 * width * we;
+  else wbase += (int64_t)s0 * W->shard_stride * we;
+  g.B = wbase;
+  g.ldb = W->ld;
+  g.C = Y->ptr;
+  g.ldc = Y->ld;
+  if (W->shard_stride == 0 && Y->shard_stride == 0) {
+    // Contiguous column shards are one product over ns * width columns: every
+    // output element is still the dot product of its own shard.
+    g.N = (int64_t)ns * width;
+    g.batch = 1;
+  } else {
+    g.N = width;
+    g.batch = ns;
+    g.sB = W->shard_stride == 0 ? width : W->shard_stride;
+    g.sC = Y->shard_stride == 0 ? width : Y->shard_stride;
+  }
+  out->g = g;
+  out->x = range_of(X->ptr, X->dtype, 1, 0, M, K, X->ld);
+  out->w = W->shard_stride == 0 ? range_of(wbase, W->dtype, 1, 0, K, (int64_t)ns * width, W->ld)
+                                : range_of(wbase, W->dtype, ns, W->shard_stride, K, width, W->ld);
+  out->y = Y->shard_stride == 0 ? range_of(Y->ptr, Y->dtype, 1, 0, M, Y->cols, Y->ld)
+                                : range_of(Y->ptr, Y->dtype, ns, Y->shard_stride, M, width, Y->ld);
+  if (overlaps(out->y, out->x) || overlaps(out->y, out->w)) return TP_ERR_ALIAS;
+  return TP_OK;
+}
+
+struct RowPlan {
+  GemmDesc g;
+  Range x, w, p;
+};
+
+// Row-parallel views: P_j = X_{s0+j} W_{s0+j}.
+tp_status plan_row(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0, int32_t ns, const tp_matrix* P,
+                   RowPlan* out) {
+  if (!X || !W || !P) return TP_ERR_NULL;
+  if (!valid_dtype(X->dtype) || !valid_dtype(W->dtype) || !valid_dtype(P->dtype)) return TP_ERR_DTYPE;
+  if (X->dtype != W->dtype || P->dtype != TP_F32) return TP_ERR_DTYPE;
+  if (X->rows < 0 || X->cols < 0 || W->rows < 0 || W->cols < 0 || P->rows < 0 || P->cols < 0) return TP_ERR_SHAPE;
+  if (N < 1 || X->cols % N != 0) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int64_t M = X->rows, K = X->cols, kb = K / N, Nout = W->cols;
+  if (W->rows != K) return TP_ERR_SHAPE;
+  if (P->rows != M || P->cols != Nout) return TP_ERR_SHAPE;
+  if (ns > 1 && P->shard_stride == 0 && M > 0 && Nout > 0) return TP_ERR_STRIDE;
+  tp_status st;
+  if ((st = check_matrix(X, ns, M, kb, K)) != TP_OK) return st;
+  if ((st = check_matrix(W, ns, kb, Nout, Nout)) != TP_OK) return st;
+  if ((st = check_matrix(P, ns, M, Nout, Nout)) != TP_OK) return st;
+
+  GemmDesc g;
+  std::memset(&g, 0, sizeof(g));
+  g.in_bf16 = X->dtype == TP_BF16;
+  g.out_kind = tp::OUT_F32;
+  g.act = tp::ACT_NONE;
+  g.M = M;
+  g.N = Nout;
+  g.K = kb;
+  g.batch = ns;
+  const int64_t e = elt_size(X->dtype);
+  g.sA = X->shard_stride == 0 ? kb : X->shard_stride;
+  g.sB = W->shard_stride == 0 ? kb * W->ld : W->shard_stride;
+  g.sC = P->shard_stride;
+  const char* xbase = static_cast<const char*>(X->ptr) + (int64_t)s0 * g.sA * e;
+  const char* wbase = static_cast<const char*>(W->ptr) + (int64_t)s0 * g.sB * e;
+  g.A = xbase;
+  g.lda = X->ld;
+  g.B = wbase;
+  g.ldb = W->ld;
+  g.C = P->ptr;
+  g.ldc = P->ld;
+  out->g = g;
+  out->x = X->shard_stride == 0 ? range_of(xbase, X->dtype, 1, 0, M, (int64_t)ns * kb, X->ld)
+                                : range_of(xbase, X->dtype, ns, X->shard_stride, M, kb, X->ld);
+  out->w = W->shard_stride == 0 ? range_of(wbase, W->dtype, 1, 0, (int64_t)ns * kb, Nout, W->ld)
+                                : range_of(wbase, W->dtype, ns, W->shard_stride, kb, Nout, W->ld);
+  out->p = range_of(P->ptr, P->dtype, ns, P->shard_stride, M, Nout, P->ld);
+  if (overlaps(out->p, out->x) || overlaps(out->p, out->w)) return TP_ERR_ALIAS;
+  return TP_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_col_linear(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0, int32_t ns, int32_t act,
+                        const tp_matrix* Y, void* stream) {
+  ColPlan plan;
+  const tp_status st = plan_col(X, W, N, s0, ns, act, Y, &plan);
+  if (st != TP_OK) return st;
+  return hip_status(run_gemm(plan.g, static_cast<hipStream_t>(stream)));
+}
+
+tp_status tp_row_linear(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0, int32_t ns,
+                        const tp_matrix* P, void* stream) {
+  RowPlan plan;
+  const tp_status st = plan_row(X, W, N, s0, ns, P, &plan);
+  if (st != TP_OK) return st;
+  return hip_status(run_gemm(plan.g, static_cast<hipStream_t>(stream)));
+}
+
+tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const tp_matrix* Y, void* stream) {
+  if (!P || !Y) return TP_ERR_NULL;
+  if (!valid_dtype(P->dtype) || !valid_dtype(Y->dtype)) return TP_ERR_DTYPE;
+  if (axis != TP_SPLIT_ROWS && axis != TP_SPLIT_COLS) return TP_ERR_SHAPE;
+  if (axis == TP_SPLIT_ROWS && P->dtype != TP_F32) return TP_ERR_DTYPE;
+  if (n < 1) return TP_ERR_INDIVISIBLE;
+  if (P->rows < 0 || P->cols < 0 || Y->rows < 0 || Y->cols < 0) return TP_ERR_SHAPE;
+  const int64_t R = P->rows, C = P->cols;
+  const int64_t ycols = axis == TP_SPLIT_ROWS ? C : (int64_t)n * C;
+  if (Y->rows != R || Y->cols != ycols) return TP_ERR_SHAPE;
+  if (Y->shard_stride != 0) return TP_ERR_STRIDE;
+  if (n > 1 && P->shard_stride == 0 && R > 0 && C > 0) return TP_ERR_STRIDE;
+  tp_status st;
+  if ((st = check_matrix(P, n, R, C, C)) != TP_OK) return st;
+  if ((st = check_matrix(Y, 1, R, ycols, ycols)) != TP_OK) return st;
+  if (overlaps(range_of(Y->ptr, Y->dtype, 1, 0, R, ycols, Y->ld),
+               range_of(P->ptr, P->dtype, n, P->shard_stride, R, C, P->ld)))
+    return TP_ERR_ALIAS;
+  CombineDesc d;
+  std::memset(&d, 0, sizeof(d));
+  d.P = P->ptr;
+  d.Y = Y->ptr;
+  d.rows = R;
+  d.cols = C;
+  d.ldp = P->ld;
+  d.sP = P->shard_stride;
+  d.ldy = Y->ld;
+  d.n = n;
+  d.p_bf16 = P->dtype == TP_BF16;
+  d.y_bf16 = Y->dtype == TP_BF16;
+  d.concat = axis == TP_SPLIT_COLS;
+  return hip_status(tp::launch_combine(d, static_cast<hipStream_t>(stream)));
+}
+
+tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, int32_t N, int32_t s0, int32_t ns,
+                 int32_t act, void* workspace, size_t* workspace_bytes, const tp_matrix* Y, void* stream) {
+  if (!X || !W1 || !W2 || !Y || !workspace_bytes) return TP_ERR_NULL;
+  if (!valid_dtype(X->dtype) || !valid_dtype(W1->dtype) || !valid_dtype(W2->dtype) || !valid_dtype(Y->dtype))
+    return TP_ERR_DTYPE;
+  if (X->dtype != W1->dtype || X->dtype != W2->dtype || Y->dtype != TP_F32) return TP_ERR_DTYPE;
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU) return TP_ERR_SHAPE;
+  if (X->rows < 0 || X->cols < 0 || W1->rows < 0 || W1->cols < 0 || W2->rows < 0 || W2->cols < 0 ||
+      Y->rows < 0 || Y->cols < 0)
+    return TP_ERR_SHAPE;
+  if (N < 1 || W1->cols % N != 0) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int64_t M = X->rows, d = X->cols, F = W1->cols, width = F / N, Dout = W2->cols;
+  if (W1->rows != d || W2->rows != F || Y->rows != M || Y->cols != Dout) return TP_ERR_SHAPE;
+  if (X->shard_stride != 0 || Y->shard_stride != 0) return TP_ERR_STRIDE;
+  // A size query (workspace == NULL) checks shapes, dtypes and strides only.
+  const bool query = workspace == nullptr;
+  tp_status st;
+  if ((st = check_matrix(X, 1, M, d, d, !query)) != TP_OK) return st;
+  if ((st = check_matrix(W1, ns, d, width, F, !query)) != TP_OK) return st;
+  if ((st = check_matrix(W2, ns, width, Dout, Dout, !query)) != TP_OK) return st;
+  if ((st = check_matrix(Y, 1, M, Dout, Dout, !query)) != TP_OK) return st;
+
+  const bool bf16 = X->dtype == TP_BF16;
+  const int32_t hdt = bf16 ? TP_BF16 : TP_F32;
+  const int64_t hcols = (int64_t)ns * width;
+
+  // Workspace: H [M, ns * width] (bf16 for bf16 inputs), then the fp32
+  // partials [ns][M][Dout] when more than one shard runs, then the skinny
+  // kernel's K-chunk sums when that kernel takes the first product.
+  size_t off_h = 0;
+  size_t bytes_h = align_up((size_t)(M * hcols * elt_size(hdt)), 256);
+  size_t off_p = bytes_h;
+  size_t bytes_p = ns > 1 ? align_up((size_t)ns * M * Dout * sizeof(float), 256) : 0;
+  size_t off_k = off_p + bytes_p;
+
+  // First product: H = act(X W1_s), columns of shard s at (s - s0) * width.
+  tp_matrix H;
+  std::memset(&H, 0, sizeof(H));
+  H.dtype = hdt;
+  H.rows = M;
+  H.cols = hcols;
+  H.ld = hcols;
+  H.shard_stride = 0;
+  ColPlan c1;
+  H.ptr = query ? nullptr : static_cast<char*>(workspace) + off_h;
+  st = plan_col(X, W1, N, s0, ns, act, &H, &c1, !query);
+  if (st == TP_ERR_ALIAS && query) st = TP_OK;  // addresses are not known in a size query
+  if (st != TP_OK) return st;
+
+  int ksplit = 1;
+  const bool skinny1 = bf16 && M <= tp::kSkinnyMaxRows && tp::gemm_skinny_supported(c1.g);
+  if (skinny1) ksplit = tp::skinny_ksplit(c1.g);
+  const size_t bytes_k = skinny1 ? align_up(tp::skinny_partial_bytes(c1.g, ksplit), 256) : 0;
+  const size_t need = off_k + bytes_k;
+  if (query) {
+    *workspace_bytes = need > 0 ? need : 256;
+    return TP_OK;
+  }
+  if (*workspace_bytes < need) return TP_ERR_WORKSPACE;
+
+  // Second product: P_j = H[:, j * width ...] W2_{s0+j}; with one shard it writes Y directly.
+  tp_matrix Hrow = H;
+  Hrow.cols = (int64_t)ns * width;  // logical K of the row split over the executed shards
+  tp_matrix Pm;
+  std::memset(&Pm, 0, sizeof(Pm));
+  Pm.dtype = TP_F32;
+  Pm.rows = M;
+  Pm.cols = Dout;
+  if (ns > 1) {
+    Pm.ptr = static_cast<char*>(workspace) + off_p;
+    Pm.ld = Dout;
+    Pm.shard_stride = M * Dout;
+  } else {
+    Pm.ptr = Y->ptr;
+    Pm.ld = Y->ld;
+    Pm.shard_stride = 0;
+  }
+  // The executed shards of W2 viewed as a row split of ns blocks, starting at block s0.
+  tp_matrix W2v = *W2;
+  if (W2->shard_stride == 0) W2v.ptr = static_cast<char*>(W2->ptr) + (int64_t)s0 * width * W2->ld * elt_size(W2->dtype);
+  else W2v.ptr = static_cast<char*>(W2->ptr) + (int64_t)s0 * W2->shard_stride * elt_size(W2->dtype);
+  W2v.rows = (int64_t)ns * width;
+  RowPlan r2;
+  if ((st = plan_row(&Hrow, &W2v, ns, 0, ns, &Pm, &r2)) != TP_OK) return st;
+
+  const Range ws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  const Range xr = range_of(X->ptr, X->dtype, 1, 0, M, d, X->ld);
+  const Range yr = range_of(Y->ptr, Y->dtype, 1, 0, M, Dout, Y->ld);
+  if (overlaps(ws, xr) || overlaps(ws, c1.w) || overlaps(ws, r2.w) || overlaps(ws, yr)) return TP_ERR_ALIAS;
+  if (overlaps(yr, xr) || overlaps(yr, c1.w) || overlaps(yr, r2.w)) return TP_ERR_ALIAS;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (skinny1) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_k);
+    e = tp::launch_gemm_skinny(c1.g, ksplit, part, s);
+    if (e == hipSuccess && ksplit > 1) e = tp::launch_skinny_finish(c1.g, ksplit, part, s);
+  } else {
+    e = run_gemm(c1.g, s);
+  }
+  if (e != hipSuccess) return TP_ERR_HIP;
+  if ((e = run_gemm(r2.g, s)) != hipSuccess) return TP_ERR_HIP;
+  if (ns > 1) {
+    CombineDesc cd;
+    std::memset(&cd, 0, sizeof(cd));
+    cd.P = Pm.ptr;
+    cd.Y = Y->ptr;
+    cd.rows = M;
+    cd.cols = Dout;
+    cd.ldp = Dout;
+    cd.sP = Pm.shard_stride;
+    cd.ldy = Y->ld;
+    cd.n = ns;
+    if ((e = tp::launch_combine(cd, s)) != hipSuccess) return TP_ERR_HIP;
+  }
+  return TP_OK;
+}
+
+const char* tp_status_string(int32_t status) {
+  switch (status) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_NULL: return "TP_ERR_NULL: a descriptor, data pointer or out-parameter is NULL";
+    case TP_ERR_DTYPE: return "TP_ERR_DTYPE: unsupported or mismatched dtype";
+    case TP_ERR_SHAPE: return "TP_ERR_SHAPE: shapes do not chain or a size is negative";
+    case TP_ERR_INDIVISIBLE: return "TP_ERR_INDIVISIBLE: the shard count must be >= 1 and divide the split dimension";
+    case TP_ERR_SHARD_RANGE: return "TP_ERR_SHARD_RANGE: need 0 <= s0, 1 <= ns, s0 + ns <= N";
+    case TP_ERR_STRIDE: return "TP_ERR_STRIDE: leading dimension or shard stride too small";
+    case TP_ERR_ALIAS: return "TP_ERR_ALIAS: an output overlaps an input";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace missing or too small";
+    case TP_ERR_HIP: return "TP_ERR_HIP: a HIP launch failed";
+    case TP_ERR_TOO_LARGE: return "TP_ERR_TOO_LARGE: a size exceeds the kernels' limits";
+    default: return "unknown tp_status";
+  }
+}
+
+int32_t tp_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+"""Host-side checks of the C interface (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/tp.h declares, and
+reject every malformed call with its status before touching HIP. The device
+pointers used here are fake: each call is built to fail validation, or is the
+workspace-size query of tp_mlp, which enqueues nothing.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tensor_sharded_linear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp.h")
+
+F32, BF16 = _lib.TP_F32, _lib.TP_BF16
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_]+)\s*\(", text)))
+
+
+def m(ptr=FAKE, dtype=BF16, rows=4, cols=8, ld=None, stride=0):
+    return _lib.matrix(ptr, dtype, rows, cols, cols if ld is None else ld, stride)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tp_version() >> 16 == 1
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.tp_status_string(code).decode().startswith(name)
+    assert lib.tp_status_string(999).decode() == "unknown tp_status"
+
+
+def col(lib, X, W, N, s0, ns, act, Y):
+    return lib.tp_col_linear(ctypes.byref(X) if X else None, ctypes.byref(W) if W else None, N, s0, ns, act,
+                             ctypes.byref(Y) if Y else None, None)
+
+
+def row(lib, X, W, N, s0, ns, P):
+    return lib.tp_row_linear(ctypes.byref(X), ctypes.byref(W), N, s0, ns, ctypes.byref(P), None)
+
+
+def test_col_linear_validation(lib):
+    # X [4, 8], W [8, 16] split in 2 -> Y [4, 16]
+    X = m(rows=4, cols=8)
+    W = m(FAKE + (1 << 20), rows=8, cols=16)
+    Y = m(FAKE + (2 << 20), rows=4, cols=16)
+    assert col(lib, None, W, 2, 0, 2, 0, Y) == 1  # NULL descriptor
+    assert col(lib, m(dtype=7), W, 2, 0, 2, 0, Y) == 2  # bad dtype
+    assert col(lib, m(dtype=F32), W, 2, 0, 2, 0, Y) == 2  # X/W dtype mismatch
+    assert col(lib, m(rows=4, cols=6), W, 2, 0, 2, 0, Y) == 3  # X.cols != W.rows
+    assert col(lib, X, W, 2, 0, 2, 0, m(FAKE + (2 << 20), rows=4, cols=8)) == 3  # Y.cols != ns*Nout/N
+    assert col(lib, X, W, 3, 0, 3, 0, Y) == 4  # 3 does not divide 16
+    assert col(lib, X, W, 0, 0, 1, 0, Y) == 4  # N < 1
+    assert col(lib, X, W, 2, 1, 2, 0, Y) == 5  # s0 + ns > N
+    assert col(lib, X, W, 2, -1, 1, 0, Y) == 5
+    assert col(lib, X, W, 2, 0, 0, 0, Y) == 5
+    assert col(lib, X, m(FAKE + (1 << 20), rows=8, cols=16, ld=15), 2, 0, 2, 0, Y) == 6  # ld < row
+    assert col(lib, m(rows=4, cols=8, stride=64), W, 2, 0, 2, 0, Y) == 6  # X may not be shard-major
+    # shard-major W whose blocks overlap: blocks [8, 8] need stride >= 7*8+8 = 64
+    assert col(lib, X, m(FAKE + (1 << 20), rows=8, cols=16, ld=8, stride=32), 2, 0, 2, 0, Y) == 6
+    assert col(lib, X, W, 2, 0, 2, 0, m(FAKE + 16, rows=4, cols=16)) == 7  # Y overlaps X
+    assert col(lib, X, W, 2, 0, 2, 5, Y) == 3  # unknown activation
+    assert col(lib, X, m(0, rows=8, cols=16), 2, 0, 2, 0, Y) == 1  # NULL data pointer
+
+
+def test_row_linear_validation(lib):
+    X = m(rows=4, cols=8)
+    W = m(FAKE + (1 << 20), rows=8, cols=16)
+    P = m(FAKE + (2 << 20), dtype=F32, rows=4, cols=16, stride=64)
+    assert row(lib, X, W, 2, 0, 2, m(FAKE + (2 << 20), dtype=BF16, rows=4, cols=16, stride=64)) == 2  # P not fp32
+    assert row(lib, X, W, 3, 0, 3, P) == 4  # 3 does not divide K = 8
+    assert row(lib, X, m(FAKE + (1 << 20), rows=6, cols=16), 2, 0, 2, P) == 3  # W.rows != K
+    assert row(lib, X, W, 2, 0, 2, m(FAKE + (2 << 20), dtype=F32, rows=4, cols=16, stride=0)) == 6  # P overlap
+    assert row(lib, X, W, 2, 0, 2, m(FAKE + (2 << 20), dtype=F32, rows=4, cols=16, stride=32)) == 6
+    assert row(lib, X, W, 2, 2, 1, P) == 5
+    assert row(lib, X, W, 2, 0, 2, m(FAKE + 8, dtype=F32, rows=4, cols=16, stride=64)) == 7  # P over X
+
+
+def test_reduce_validation(lib):
+    P = m(FAKE, dtype=F32, rows=4, cols=16, stride=64)
+    Y = m(FAKE + (1 << 20), dtype=F32, rows=4, cols=16)
+    red = lib.tp_reduce_partials
+    assert red(None, 2, 1, ctypes.byref(Y), None) == 1
+    assert red(ctypes.byref(m(FAKE, dtype=BF16, rows=4, cols=16, stride=64)), 2, 1, ctypes.byref(Y), None) == 2
+    assert red(ctypes.byref(P), 0, 1, ctypes.byref(Y), None) == 4
+    assert red(ctypes.byref(P), 2, 7, ctypes.byref(Y), None) == 3  # bad axis
+    assert red(ctypes.byref(P), 2, 0, ctypes.byref(Y), None) == 3  # concat needs Y.cols = 32
+    assert red(ctypes.byref(P), 2, 1, ctypes.byref(m(FAKE + (1 << 20), dtype=F32, rows=4, cols=16, stride=8)),
+               None) == 6
+    assert red(ctypes.byref(m(FAKE, dtype=F32, rows=4, cols=16, stride=16)), 2, 1, ctypes.byref(Y), None) == 6
+    assert red(ctypes.byref(P), 2, 1, ctypes.byref(m(FAKE + 64, dtype=F32, rows=4, cols=16)), None) == 7
+
+
+def mlp_query(lib, X, W1, W2, N, s0, ns, Y):
+    size = ctypes.c_size_t(0)
+    st = lib.tp_mlp(ctypes.byref(X), ctypes.byref(W1), ctypes.byref(W2), N, s0, ns, 1, None, ctypes.byref(size),
+                    ctypes.byref(Y), None)
+    return st, size.value
+
+
+def test_mlp_validation_and_workspace_query(lib):
+    M, d, F, N = 64, 32, 128, 4
+    X = m(FAKE, rows=M, cols=d)
+    W1 = m(FAKE + (1 << 20), rows=d, cols=F)
+    W2 = m(FAKE + (2 << 20), rows=F, cols=d)
+    Y = m(FAKE + (3 << 20), dtype=F32, rows=M, cols=d)
+    st, size = mlp_query(lib, X, W1, W2, N, 0, N, Y)
+    assert st == 0
+    # H bf16 [64, 128] + fp32 partials [4][64][32], each rounded up to 256 bytes
+    assert size == 64 * 128 * 2 + 4 * 64 * 32 * 4
+    st, size1 = mlp_query(lib, X, W1, W2, N, 1, 1, Y)
+    assert st == 0 and size1 == 64 * 32 * 2  # one shard writes Y directly: only H
+    assert mlp_query(lib, X, W1, W2, 3, 0, 3, Y)[0] == 4
+    assert mlp_query(lib, X, W1, W2, N, 3, 2, Y)[0] == 5
+    assert mlp_query(lib, X, W1, W2, N, 0, N, m(FAKE + (3 << 20), dtype=BF16, rows=M, cols=d))[0] == 2
+    assert mlp_query(lib, X, W1, m(FAKE + (2 << 20), rows=F, cols=d + 8), N, 0, N, Y)[0] == 3
+    size = ctypes.c_size_t(16)
+    st = lib.tp_mlp(ctypes.byref(X), ctypes.byref(W1), ctypes.byref(W2), N, 0, N, 1, ctypes.c_void_p(FAKE + (8 << 20)),
+                    ctypes.byref(size), ctypes.byref(Y), None)
+    assert st == 8  # workspace too small
+    assert lib.tp_mlp(ctypes.byref(X), ctypes.byref(W1), ctypes.byref(W2), N, 0, N, 1, None, None,
+                      ctypes.byref(Y), None) == 1
+
+
+def test_mlp_decode_workspace_includes_k_chunks(lib):
+    # 16 rows: the skinny kernel splits K; its chunk sums live in the workspace.
+    M, d, F, N = 16, 8192, 28672, 8
+    X = m(FAKE, rows=M, cols=d)
+    W1 = m(FAKE + (1 << 30), rows=d, cols=F, ld=F // N, stride=d * (F // N))
+    W2 = m(FAKE + (4 << 30), rows=F, cols=d, ld=d, stride=(F // N) * d)
+    Y = m(FAKE + (8 << 30), dtype=F32, rows=M, cols=d)
+    st, size = mlp_query(lib, X, W1, W2, N, 0, N, Y)
+    assert st == 0
+    base = 16 * 28672 * 2 + 8 * 16 * 8192 * 4
+    assert size > base
+    assert (size - base) % (16 * 28672 * 4) == 0

@@ -1,0 +1,381 @@
+"""GPU parity: the HIP path (through the C interface) against the float64 oracle.
+
+Every case draws seeded synthetic inputs (synthetic/), runs the library on
+the GPU and the oracle on the CPU on the same bits, and compares element by
+element: exactly for integer-valued inputs, else within the bars of
+tests/parity.py. Full-size workloads are checked on seeded sampled rows,
+which is exact because each output row depends only on its own input row.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_sharded_linear_amd as tp
+from synthetic import WORKLOADS, int_uniform_f32, normal_bf16, sample_rows
+from parity import assert_close, assert_exact, bf16_tensor, dev, f32_tensor, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def ints_bf16(shape, lo, hi, wid, tid):
+    """Small integers stored as bf16 (exactly representable): (bits, float32 values)."""
+    from synthetic import bf16_bits_from_f32
+
+    v = int_uniform_f32(shape, lo, hi, wid, tid)
+    return bf16_bits_from_f32(v), v
+
+
+# ----------------------------------------------------------------------------- the pages' worked example
+
+
+def test_worked_example_fp32(golden_dir):
+    with open(os.path.join(golden_dir, "worked_example.json")) as f:
+        g = json.load(f)
+    x = np.array(g["X"], np.float32)
+    w = np.array(g["W"], np.float32)
+    n = g["N"]
+    X, W = f32_tensor(x), f32_tensor(w)
+    note("worked example: tp_col_linear concat, N=2, fp32")
+    assert_exact(host(tp.col_linear(X, W, n)), np.array(g["Y"]), "column split, concatenated")
+    note("worked example: tp_col_linear partitioned")
+    parts = host(tp.col_linear(X, W, n, partitioned=True))
+    for s in range(n):
+        assert_exact(parts[s], np.array(g["col_shard_outputs"][s]), f"column shard {s}")
+    note("worked example: tp_row_linear + tp_reduce_partials")
+    P = tp.row_linear(X, W, n)
+    ph = host(P)
+    for s in range(n):
+        assert_exact(ph[s], np.array(g["row_partials"][s]), f"row partial {s}")
+    assert_exact(host(tp.reduce_partials(P, "rows")), np.array(g["Y"]), "row partials summed")
+    note("worked example: tp_reduce_partials concat of the column shards")
+    cparts = tp.col_linear(X, W, n, partitioned=True)
+    assert_exact(host(tp.reduce_partials(cparts, "cols")), np.array(g["Y"]), "column shards concatenated")
+
+
+# ----------------------------------------------------------------------------- the tiny split check (exact)
+
+
+def test_split_check_fp32_exact():
+    wl = WORKLOADS["split_check"]
+    x = int_uniform_f32((wl.M, wl.d), -4, 4, wl.wid, 0)
+    w = int_uniform_f32((wl.d, wl.F), -4, 4, wl.wid, 1)
+    X, W = f32_tensor(x), f32_tensor(w)
+    ref = oracle.matmul(x, w)
+    note("split check fp32: column split N=2")
+    assert_exact(host(tp.col_linear(X, W, 2)), oracle.col_linear(x, w, 2), "column split")
+    outs = host(tp.col_linear(X, W, 2, partitioned=True))
+    for s, o in enumerate(oracle.col_shard_outputs(x, w, 2)):
+        assert_exact(outs[s], o, f"column shard {s}")
+    note("split check fp32: row split N=2")
+    P = tp.row_linear(X, W, 2)
+    for s, p in enumerate(oracle.row_partials(x, w, 2)):
+        assert_exact(host(P)[s], p, f"row partial {s}")
+    assert_exact(host(tp.reduce_partials(P)), oracle.row_linear(x, w, 2), "row split summed")
+    assert_exact(host(tp.reduce_partials(P)), ref, "equals the unsharded product")
+
+
+def test_split_check_bf16_exact():
+    """The same integers in bf16 take the matrix-core kernels (few rows: the skinny kernel)."""
+    wl = WORKLOADS["split_check"]
+    xb, x = ints_bf16((wl.M, wl.d), -4, 4, wl.wid, 0)
+    wb, w = ints_bf16((wl.d, wl.F), -4, 4, wl.wid, 1)
+    X, W = bf16_tensor(xb), bf16_tensor(wb)
+    note("split check bf16: column split, fp32 out")
+    assert_exact(host(tp.col_linear(X, W, 2, out_dtype=torch.float32)), oracle.col_linear(x, w, 2), "column")
+    note("split check bf16: row split")
+    P = tp.row_linear(X, W, 2)
+    assert_exact(host(tp.reduce_partials(P)), oracle.row_linear(x, w, 2), "row")
+
+
+# ----------------------------------------------------------------------------- large-tile kernel
+
+
+@pytest.mark.parametrize("M,K,width,N", [(300, 264, 264, 2), (512, 512, 256, 4), (257, 64, 40, 3), (1, 8, 256, 1)])
+def test_mfma_exact_integers(M, K, width, N):
+    """Integer bf16 inputs through the large-tile kernel: fp32 results must be exact."""
+    nout = width * N
+    xb, x = ints_bf16((M, K), -2, 2, 90 + M, 0)
+    wb, w = ints_bf16((K, nout), -2, 2, 90 + M, 1)
+    X, W = bf16_tensor(xb), bf16_tensor(wb)
+    note(f"mfma exact: col M={M} K={K} width={width} N={N}")
+    assert_exact(host(tp.col_linear(X, W, N, out_dtype=torch.float32)), oracle.col_linear(x, w, N), "column")
+    if K % N == 0:
+        note(f"mfma exact: row M={M} K={K} Nout={nout} N={N}")
+        P = tp.row_linear(X, W, N)
+        for s, p in enumerate(oracle.row_partials(x, w, N)):
+            assert_exact(host(P[s]), p, f"row partial {s}")
+
+
+@pytest.mark.parametrize("M,K,width,N,act", [
+    (600, 520, 392, 2, "none"),
+    (600, 520, 392, 2, "gelu"),
+    (256, 1024, 256, 4, "gelu"),
+    (777, 136, 136, 3, "none"),
+])
+def test_mfma_float_col(M, K, width, N, act):
+    nout = width * N
+    xb, x = normal_bf16((M, K), 1.0, 200 + M, 0)
+    wb, w = normal_bf16((K, nout), 0.02, 200 + M, 1)
+    X, W = bf16_tensor(xb), bf16_tensor(wb)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        note(f"mfma col M={M} K={K} width={width} N={N} act={act} out={out_dtype}")
+        got = host(tp.col_linear(X, W, N, act=act, out_dtype=out_dtype))
+        assert_close(got, oracle.col_linear(x, w, N, act), f"col {act} {out_dtype}",
+                     stored_bf16=out_dtype == torch.bfloat16)
+    # a proper sub-range of shards, partitioned output
+    if N >= 2:
+        note(f"mfma col sub-range s0=1 ns={N - 1} partitioned")
+        got = host(tp.col_linear(X, W, N, s0=1, ns=N - 1, act=act, partitioned=True, out_dtype=torch.float32))
+        for j, o in enumerate(oracle.col_shard_outputs(x, w, N, act, s0=1, ns=N - 1)):
+            assert_close(got[j], o, f"col shard {j + 1}")
+
+
+@pytest.mark.parametrize("M,K,Nout,N", [(600, 1040, 392, 2), (300, 512, 768, 4), (1000, 96, 264, 3)])
+def test_mfma_float_row(M, K, Nout, N):
+    xb, x = normal_bf16((M, K), 1.0, 300 + M, 0)
+    wb, w = normal_bf16((K, Nout), 0.02, 300 + M, 1)
+    X, W = bf16_tensor(xb), bf16_tensor(wb)
+    note(f"mfma row M={M} K={K} Nout={Nout} N={N}")
+    P = tp.row_linear(X, W, N)
+    ph = host(P)
+    for s, p in enumerate(oracle.row_partials(x, w, N)):
+        assert_close(ph[s], p, f"row partial {s}")
+    assert_close(host(tp.reduce_partials(P)), oracle.row_linear(x, w, N), "row sum")
+
+
+def test_shard_major_weights_and_inputs():
+    """3-D shard-major stacks (block s at base + s * stride) for both splits."""
+    M, K, width, N = 320, 256, 128, 4
+    xb, x = normal_bf16((M, K), 1.0, 400, 0)
+    wb, w = normal_bf16((N, K, width), 0.02, 400, 1)  # column blocks
+    X, W = bf16_tensor(xb), bf16_tensor(wb)
+    wfull = np.concatenate(list(w), axis=1)
+    note("shard-major column weights")
+    assert_close(host(tp.col_linear(X, W, N, out_dtype=torch.float32)), oracle.col_linear(x, wfull, N), "col")
+    # row split with a shard-major input (the partitioned output of a column layer)
+    xsb, xs = normal_bf16((N, M, 64), 1.0, 401, 0)
+    w2b, w2 = normal_bf16((N, 64, 200), 0.02, 401, 1)
+    note("shard-major row inputs and weights")
+    P = tp.row_linear(bf16_tensor(xsb), bf16_tensor(w2b), N)
+    xfull = np.concatenate(list(xs), axis=1)
+    w2full = np.concatenate(list(w2), axis=0)
+    for s, p in enumerate(oracle.row_partials(xfull, w2full, N)):
+        assert_close(host(P[s]), p, f"row partial {s}")
+
+
+# ----------------------------------------------------------------------------- guarded kernel
+
+
+def test_generic_path_unaligned_strides():
+    """Leading dimensions that are not multiples of 8 take the element-guarded kernel."""
+    M, K, width, N = 70, 37, 21, 3
+    xb, x = normal_bf16((M, K + 3), 1.0, 500, 0)  # row stride K+3, view of the first K columns
+    wb, w = normal_bf16((K, width * N + 5), 0.02, 500, 1)
+    X = bf16_tensor(xb)[:, :K]
+    W = bf16_tensor(wb)[:, : width * N]
+    note("generic path: bf16 unaligned col")
+    got = host(tp.col_linear(X, W, N, act="gelu", out_dtype=torch.float32))
+    assert_close(got, oracle.col_linear(x[:, :K], w[:, : width * N], N, "gelu"), "generic col")
+    xi = int_uniform_f32((M, 36), -4, 4, 501, 0)
+    wi = int_uniform_f32((36, 50), -4, 4, 501, 1)
+    note("generic path: fp32 exact row")
+    P = tp.row_linear(f32_tensor(xi), f32_tensor(wi), 4)
+    assert_exact(host(tp.reduce_partials(P)), oracle.row_linear(xi, wi, 4), "generic row exact")
+
+
+# ----------------------------------------------------------------------------- skinny kernel
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 17, 32])
+def test_skinny_col_and_row(M):
+    K, width, N = 1000, 192, 3
+    xb, x = normal_bf16((M, K), 1.0, 600 + M, 0)
+    wb, w = normal_bf16((K, width * N), 0.02, 600 + M, 1)
+    X, W = bf16_tensor(xb), bf16_tensor(wb)
+    note(f"skinny col M={M} K={K} width={width} N={N}")
+    got = host(tp.col_linear(X, W, N, act="gelu", out_dtype=torch.float32))
+    assert_close(got, oracle.col_linear(x, w, N, "gelu"), f"skinny col M={M}")
+    Kr = 1200
+    xb2, x2 = normal_bf16((M, Kr), 1.0, 650 + M, 0)
+    wb2, w2 = normal_bf16((Kr, 264), 0.02, 650 + M, 1)
+    note(f"skinny row M={M} K={Kr} N={N}")
+    P = tp.row_linear(bf16_tensor(xb2), bf16_tensor(wb2), N)
+    for s, p in enumerate(oracle.row_partials(x2, w2, N)):
+        assert_close(host(P[s]), p, f"skinny row partial {s}")
+
+
+def test_skinny_exact_integers():
+    M, K, width, N = 16, 2048, 64, 4
+    xb, x = ints_bf16((M, K), -1, 1, 700, 0)
+    wb, w = ints_bf16((K, width * N), -2, 2, 700, 1)
+    note("skinny exact integers")
+    got = host(tp.col_linear(bf16_tensor(xb), bf16_tensor(wb), N, out_dtype=torch.float32))
+    assert_exact(got, oracle.col_linear(x, w, N), "skinny col exact")
+
+
+# ----------------------------------------------------------------------------- combine kernels
+
+
+@pytest.mark.parametrize("rows,cols,n", [(33, 64, 3), (5, 7, 4), (128, 1000, 8), (1, 4, 1)])
+def test_reduce_and_concat(rows, cols, n):
+    g = np.random.default_rng(rows * 1000 + cols)
+    p = g.standard_normal((n, rows, cols)).astype(np.float32)
+    P = f32_tensor(p)
+    note(f"reduce rows={rows} cols={cols} n={n}")
+    got = host(tp.reduce_partials(P, "rows"))
+    assert_close(got, oracle.reduce_sum(list(p)), "sum")
+    # the fp32 sum in ascending shard order is reproduced exactly by sequential float32 adds
+    seq = p[0].copy()
+    for j in range(1, n):
+        seq = (seq + p[j]).astype(np.float32)
+    assert_exact(got, seq, "ascending-order fp32 sum")
+    got16 = host(tp.reduce_partials(P, "rows", out_dtype=torch.bfloat16))
+    assert_close(got16, oracle.reduce_sum(list(p)), "sum bf16 out", stored_bf16=True)
+    note(f"concat rows={rows} cols={cols} n={n}")
+    assert_exact(host(tp.reduce_partials(P, "cols")), oracle.concat_cols(list(p)), "concat")
+
+
+# ----------------------------------------------------------------------------- MLP chain
+
+
+def test_mlp_exact_integers_no_activation():
+    M, d, F, N = 96, 256, 512, 4
+    xb, x = ints_bf16((M, d), -1, 1, 800, 0)
+    w1b, w1 = ints_bf16((d, F), -1, 1, 800, 1)
+    w2b, w2 = ints_bf16((F, d), -1, 1, 800, 2)
+    note("mlp exact, act none, N=4")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), N, act="none"))
+    assert_exact(got, oracle.mlp(x, w1, w2, N, "none"), "mlp exact")
+    note("mlp exact, act none, decode rows")
+    got = host(tp.mlp(bf16_tensor(xb[:16]), bf16_tensor(w1b), bf16_tensor(w2b), N, act="none"))
+    assert_exact(got, oracle.mlp(x[:16], w1, w2, N, "none"), "mlp exact decode")
+
+
+@pytest.mark.parametrize("M,d,F,N,s0,ns", [(300, 512, 2048, 4, 0, 4), (300, 512, 2048, 4, 1, 2),
+                                           (16, 1024, 4096, 8, 0, 8), (9, 512, 1536, 3, 0, 3),
+                                           (256, 256, 1024, 1, 0, 1)])
+def test_mlp_gelu(M, d, F, N, s0, ns):
+    xb, x = normal_bf16((M, d), 1.0, 900 + M, 0)
+    w1b, w1 = normal_bf16((d, F), 0.02, 900 + M, 1)
+    w2b, w2 = normal_bf16((F, d), 0.02, 900 + M, 2)
+    note(f"mlp gelu M={M} d={d} F={F} N={N} s0={s0} ns={ns}")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), N, s0=s0, ns=ns))
+    assert_close(got, oracle.mlp(x, w1, w2, N, "gelu", s0, ns), "mlp gelu")
+
+
+def test_mlp_fp32_exact():
+    M, d, F, N = 8, 24, 36, 3
+    x = int_uniform_f32((M, d), -2, 2, 950, 0)
+    w1 = int_uniform_f32((d, F), -2, 2, 950, 1)
+    w2 = int_uniform_f32((F, d), -2, 2, 950, 2)
+    note("mlp fp32 exact act none")
+    got = host(tp.mlp(f32_tensor(x), f32_tensor(w1), f32_tensor(w2), N, act="none"))
+    assert_exact(got, oracle.mlp(x, w1, w2, N, "none"), "fp32 mlp")
+
+
+def test_empty_and_degenerate():
+    xb, x = normal_bf16((0, 64), 1.0, 960, 0)
+    wb, w = normal_bf16((64, 128), 0.02, 960, 1)
+    note("empty M")
+    out = tp.col_linear(bf16_tensor(xb), bf16_tensor(wb), 2)
+    assert out.shape == (0, 128)
+    # K = 0: the product is empty, so every output is act(0) = 0
+    note("K = 0")
+    X0 = torch.zeros((5, 0), dtype=torch.bfloat16, device=dev())
+    W0 = torch.zeros((0, 16), dtype=torch.bfloat16, device=dev())
+    got = host(tp.col_linear(X0, W0, 2, out_dtype=torch.float32, act="gelu"))
+    assert_exact(got, np.zeros((5, 16)), "K=0")
+    # one column per shard (N = Nout)
+    xb, x = normal_bf16((40, 64), 1.0, 961, 0)
+    wb, w = normal_bf16((64, 8), 0.02, 961, 1)
+    note("N = Nout: one column per shard")
+    got = host(tp.col_linear(bf16_tensor(xb), bf16_tensor(wb), 8, out_dtype=torch.float32))
+    assert_close(got, oracle.col_linear(x, w, 8), "one column per shard")
+
+
+def test_determinism_bitwise():
+    M, d, F, N = 512, 1024, 4096, 8
+    xb, _ = normal_bf16((M, d), 1.0, 970, 0)
+    w1b, _ = normal_bf16((d, F), 0.02, 970, 1)
+    w2b, _ = normal_bf16((F, d), 0.02, 970, 2)
+    X, W1, W2 = bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b)
+    note("determinism: two mlp runs")
+    a = tp.mlp(X, W1, W2, N).clone()
+    b = tp.mlp(X, W1, W2, N).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    note("determinism: decode rows")
+    a = tp.mlp(X[:16], W1, W2, N).clone()
+    b = tp.mlp(X[:16], W1, W2, N).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+
+def _rows(m):
+    return sample_rows(m, 256, seed=m)
+
+
+def test_megatron_mlp_full_size():
+    wl = WORKLOADS["megatron_mlp"]
+    xb, x = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)
+    w1b, w1 = normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)
+    w2b, w2 = normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)
+    note("megatron mlp full size: X [2048,4096], W1 [4096,16384], W2 [16384,4096], N=8, all shards")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), wl.N))
+    rows = _rows(wl.M)
+    assert_close(got[rows], oracle.mlp(x[rows], w1, w2, wl.N, "gelu"), "megatron mlp sampled rows")
+
+
+def test_attention_projections_full_size():
+    wl = WORKLOADS["attn_proj"]
+    xb, x = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)
+    wqb, wq = normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)
+    wob, wo = normal_bf16((wl.d, wl.out), 0.02, wl.wid, 2)
+    ab, a = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 3)
+    rows = _rows(wl.M)
+    note("attention QKV column-parallel full size: X [4096,8192] Wqkv [8192,24576] N=8 -> bf16")
+    qkv = host(tp.col_linear(bf16_tensor(xb), bf16_tensor(wqb), wl.N))
+    assert_close(qkv[rows], oracle.col_linear(x[rows], wq, wl.N), "qkv sampled rows", stored_bf16=True)
+    del qkv
+    note("attention output projection row-parallel full size: A [4096,8192] Wo [8192,8192] N=8")
+    P = tp.row_linear(bf16_tensor(ab), bf16_tensor(wob), wl.N)
+    Y = host(tp.reduce_partials(P))
+    parts = oracle.row_partials(a[rows], wo, wl.N)
+    Pr = host(P[:, torch.as_tensor(rows, device=P.device)])
+    for s in range(wl.N):
+        assert_close(Pr[s], parts[s], f"W_o partial {s}")
+    assert_close(Y[rows], oracle.reduce_sum(parts), "W_o reduced")
+
+
+def test_gpt3_mlp_one_shard_full_size():
+    wl = WORKLOADS["gpt3_mlp_shard"]
+    width = wl.F // wl.N
+    xb, x = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)
+    w1b, w1 = normal_bf16((1, wl.d, width), 0.02, wl.wid, 1)   # shard 0 of W1 only
+    w2b, w2 = normal_bf16((1, width, wl.d), 0.02, wl.wid, 2)   # shard 0 of W2 only
+    note("gpt3-width mlp, shard 0 of 8: X [16384,12288], W1_0 [12288,6144], W2_0 [6144,12288]")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), wl.N, s0=0, ns=1))
+    rows = _rows(wl.M)
+    # shard 0 of an 8-way split is the whole of the stored block
+    ref = oracle.mlp_shard_partials(x[rows], w1[0], w2[0], 1, "gelu")[0]
+    assert_close(got[rows], ref, "gpt3 shard partial sampled rows")
+
+
+def test_decode_mlp_full_size():
+    wl = WORKLOADS["decode_mlp"]
+    width = wl.F // wl.N
+    xb, x = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)
+    w1b, w1 = normal_bf16((wl.N, wl.d, width), 0.02, wl.wid, 1)
+    w2b, w2 = normal_bf16((wl.N, width, wl.d), 0.02, wl.wid, 2)
+    note("decode mlp full size: X [16,8192], W1 8x[8192,3584], W2 8x[3584,8192]")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), wl.N))
+    w1full = np.concatenate(list(w1), axis=1)
+    w2full = np.concatenate(list(w2), axis=0)
+    assert_close(got, oracle.mlp(x, w1full, w2full, wl.N, "gelu"), "decode mlp")
