@@ -141,8 +141,22 @@ def test_mlp_validation_and_workspace_query(lib):
                       ctypes.byref(Y), None) == 1
 
 
-def test_mlp_decode_workspace_includes_k_chunks(lib):
-    # 16 rows: the skinny kernel splits K; its chunk sums live in the workspace.
+def test_mlp_narrow_decode_workspace_includes_k_chunks(lib):
+    # 16 rows and narrow shards (few column tiles): the skinny kernel splits K
+    # to fill the GPU, and its chunk sums live in the workspace.
+    M, d, F, N = 16, 8192, 2048, 8
+    X = m(FAKE, rows=M, cols=d)
+    W1 = m(FAKE + (1 << 30), rows=d, cols=F, ld=F // N, stride=d * (F // N))
+    W2 = m(FAKE + (4 << 30), rows=F, cols=d, ld=d, stride=(F // N) * d)
+    Y = m(FAKE + (8 << 30), dtype=F32, rows=M, cols=d)
+    st, size = mlp_query(lib, X, W1, W2, N, 0, N, Y)
+    assert st == 0
+    base = M * F * 2 + N * M * d * 4
+    assert size > base
+    assert (size - base) % (M * F * 4) == 0
+
+
+def test_mlp_decode_workspace_covers_intermediate_and_partials(lib):
     M, d, F, N = 16, 8192, 28672, 8
     X = m(FAKE, rows=M, cols=d)
     W1 = m(FAKE + (1 << 30), rows=d, cols=F, ld=F // N, stride=d * (F // N))
@@ -150,6 +164,4 @@ def test_mlp_decode_workspace_includes_k_chunks(lib):
     Y = m(FAKE + (8 << 30), dtype=F32, rows=M, cols=d)
     st, size = mlp_query(lib, X, W1, W2, N, 0, N, Y)
     assert st == 0
-    base = 16 * 28672 * 2 + 8 * 16 * 8192 * 4
-    assert size > base
-    assert (size - base) % (16 * 28672 * 4) == 0
+    assert size >= M * F * 2 + N * M * d * 4

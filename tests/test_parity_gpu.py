@@ -217,6 +217,30 @@ def test_skinny_exact_integers():
     assert_exact(got, oracle.col_linear(x, w, N), "skinny col exact")
 
 
+def test_skinny_wide_tiles_ragged():
+    # Enough column tiles (>= 192 of 256 columns) that the skinny kernel takes
+    # its 256-column tiles; the column count leaves a ragged last tile and the
+    # per-shard K (264) a partial 32-row slice.
+    M, K, Nout, N = 5, 2112, 6000, 8
+    xb, x = normal_bf16((M, K), 1.0, 720, 0)
+    wb, w = normal_bf16((K, Nout), 0.02, 720, 1)
+    note(f"skinny wide row M={M} K={K} Nout={Nout} N={N}")
+    P = tp.row_linear(bf16_tensor(xb), bf16_tensor(wb), N)
+    for s, p in enumerate(oracle.row_partials(x, w, N)):
+        assert_close(host(P[s]), p, f"skinny wide row partial {s}")
+    xi, xf = ints_bf16((M, K), -1, 1, 721, 0)
+    wi, wf = ints_bf16((K, Nout), -2, 2, 721, 1)
+    P = tp.row_linear(bf16_tensor(xi), bf16_tensor(wi), N)
+    for s, p in enumerate(oracle.row_partials(xf, wf, N)):
+        assert_exact(host(P[s]), p, f"skinny wide row exact partial {s}")
+    M2, K2, width = 16, 96, 6144
+    xb2, x2 = normal_bf16((M2, K2), 1.0, 722, 0)
+    wb2, w2 = normal_bf16((K2, width * N), 0.02, 722, 1)
+    note(f"skinny wide col gelu M={M2} K={K2} Nout={width * N}")
+    got = host(tp.col_linear(bf16_tensor(xb2), bf16_tensor(wb2), N, act="gelu", out_dtype=torch.float32))
+    assert_close(got, oracle.col_linear(x2, w2, N, "gelu"), "skinny wide col gelu")
+
+
 # ----------------------------------------------------------------------------- combine kernels
 
 
