@@ -27,11 +27,26 @@ __global__ __launch_bounds__(256) void sum_vec4_kernel(CombineDesc d) {
   const int64_t c4 = d.cols >> 2;
   const int64_t total = d.rows * c4;
   const float* P = static_cast<const float*>(d.P);
+  const int n = d.n;
   for (int64_t i = thread_index(); i < total; i += grid_threads()) {
     const int64_t r = i / c4, c = (i - r * c4) << 2;
-    const float* src = P + r * d.ldp + c;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
-    for (int j = 1; j < d.n; ++j) acc += *reinterpret_cast<const f32x4*>(src + (int64_t)j * d.sP);
+    const f32x4* src = reinterpret_cast<const f32x4*>(P + r * d.ldp + c);
+    const int64_t step = d.sP >> 2;  // shard stride in 16-byte vectors
+    // The partials are read once: nontemporal loads, four shards in flight at
+    // a time, added strictly in ascending shard order.
+    f32x4 acc = __builtin_nontemporal_load(src);
+    int j = 1;
+    for (; j + 4 <= n; j += 4) {
+      const f32x4 a = __builtin_nontemporal_load(src + (int64_t)j * step);
+      const f32x4 b = __builtin_nontemporal_load(src + (int64_t)(j + 1) * step);
+      const f32x4 e = __builtin_nontemporal_load(src + (int64_t)(j + 2) * step);
+      const f32x4 f = __builtin_nontemporal_load(src + (int64_t)(j + 3) * step);
+      acc += a;
+      acc += b;
+      acc += e;
+      acc += f;
+    }
+    for (; j < n; ++j) acc += __builtin_nontemporal_load(src + (int64_t)j * step);
     if (YBF16) {
       bf16x4 h;
       h[0] = (__bf16)acc[0]; h[1] = (__bf16)acc[1]; h[2] = (__bf16)acc[2]; h[3] = (__bf16)acc[3];

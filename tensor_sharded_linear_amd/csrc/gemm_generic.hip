@@ -12,10 +12,6 @@ namespace {
 
 constexpr int TM = 64, TN = 64, TK = 16;
 
-__device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
-}
-
 template <typename T>
 __device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
   return (float)static_cast<const T*>(p)[i];
@@ -71,7 +67,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d, int tiles
       const int64_t gn = n0 + tx + 16 * j;
       if (gm < d.M && gn < d.N) {
         float v = acc[i][j];
-        if (ACT == ACT_GELU) v = gelu_erf(v);
+        if (ACT == ACT_GELU) v = gelu(v);
         const int64_t off = z * d.sC + gm * d.ldc + gn;
         if (OUT == OUT_F32) static_cast<float*>(d.C)[off] = v;
         else static_cast<__bf16*>(d.C)[off] = (__bf16)v;

@@ -72,10 +72,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // further on (the next 16-lane group) move to the other half of the window.
 __device__ __forceinline__ int swz_w(int r) { return (2 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
 
-__device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
-}
-
 template <int SBN, int MT, int OUT, int ACT, bool PARTIAL>
 __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(SkParams p) {
   using T = Tile<SBN>;
@@ -193,7 +189,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(SkParams p) {
         if (PARTIAL) {
           p.part[(((int64_t)c * d.batch + z) * M + row) * N + gn] = v;
         } else {
-          if (ACT == ACT_GELU) v = gelu_erf(v);
+          if (ACT == ACT_GELU) v = gelu(v);
           const int64_t off = z * d.sC + row * d.ldc + gn;
           if (OUT == OUT_F32) static_cast<float*>(d.C)[off] = v;
           else static_cast<__bf16*>(d.C)[off] = (__bf16)v;
@@ -213,7 +209,7 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(GemmDesc d, int kspl
     const int64_t m = rem / d.N, n = rem - m * d.N;
     float v = part[idx];
     for (int c = 1; c < ksplit; ++c) v += part[(int64_t)c * total + idx];
-    if (ACT == ACT_GELU) v = gelu_erf(v);
+    if (ACT == ACT_GELU) v = gelu(v);
     const int64_t off = z * d.sC + m * d.ldc + n;
     if (OUT == OUT_F32) static_cast<float*>(d.C)[off] = v;
     else static_cast<__bf16*>(d.C)[off] = (__bf16)v;
