@@ -24,6 +24,9 @@ loops on small integer inputs, the split invariants for every shard count
 dividing the split dimension, textbook values of the normal CDF for GeLU and
 an independent Taylor-series error function, and mutation tests that plant
 plausible mistakes here and check that a pin catches each one.
+The backward functions are pinned against central finite differences of the
+forward functions above, against the unsharded gradients for every shard
+count, against brute force, and by their own mutation tests.
 Readings where the pages are silent: W is [in, out] row-major and Y = X W;
 blocks are contiguous and shard s takes the s-th; N must divide the split
 dimension; the MLP activation is the exact GeLU x * Phi(x); the intermediate
@@ -51,6 +54,13 @@ __all__ = [
     "row_linear",
     "mlp_shard_partials",
     "mlp",
+    "transpose",
+    "gelu_grad",
+    "act_grad",
+    "split_cols",
+    "col_linear_backward",
+    "row_linear_backward",
+    "mlp_backward",
 ]
 
 ACTS = ("none", "gelu")
@@ -201,3 +211,96 @@ def mlp_shard_partials(x, w1, w2, n: int, act: str = "gelu", s0: int = 0, ns: in
 def mlp(x, w1, w2, n: int, act: str = "gelu", s0: int = 0, ns: int | None = None) -> np.ndarray:
     """Y = sum_s act(X W1_s) W2_s, the single sum closing the MLP pair."""
     return reduce_sum(mlp_shard_partials(x, w1, w2, n, act, s0, ns))
+
+
+# ----------------------------------------------------------------------------- backward passes
+#
+# The pages pair each forward collective with one in the backward pass
+# ([TP-topic] "Megatron-LM Tensor Parallelism": identity operators of the
+# forward pass become all-reduces in the backward pass and the reverse;
+# "Communication Optimization": gradients are all-reduced with the forward
+# volume; "Memory Distribution": each shard computes the gradients of its own
+# 1/N of the weights). They do not write the gradients out; the ones below are
+# the chain rule for Y = X W: with dY the gradient of a loss with respect to Y,
+# the gradient with respect to X is dY W^T and with respect to W is X^T dY.
+
+
+def transpose(a) -> np.ndarray:
+    """The transposed matrix (rows become columns), float64."""
+    return widen(a).T
+
+
+def gelu_grad(x) -> np.ndarray:
+    """Derivative of the exact GeLU: Phi(x) + x phi(x), phi(x) = exp(-x^2/2) / sqrt(2 pi), float64."""
+    x = widen(x)
+    return 0.5 * (1.0 + _erf(x / np.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+
+
+def act_grad(z, act: str) -> np.ndarray:
+    if act == "none":
+        return np.ones_like(widen(z))
+    if act == "gelu":
+        return gelu_grad(z)
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def split_cols(y, ns: int):
+    """The ns equal column blocks of y, in order (the inverse of concat_cols)."""
+    y = widen(y)
+    width = _check_split(y.shape[1], ns, "columns")
+    return [y[:, j * width:(j + 1) * width] for j in range(ns)]
+
+
+def col_linear_backward(x, w, dy, n: int, s0: int = 0, ns: int | None = None):
+    """Backward of the column split (no activation).
+
+    X reaches every shard unchanged in the forward pass, so its gradient is the
+    sum of the shards' contributions (the backward all-reduce):
+        dX = sum_j P_j, P_j = dY_j W_s^T;   dW_s = X^T dY_j   (j = s - s0).
+    dy is [M, ns*Nout/N] (shard j's block at columns j*Nout/N).
+    Returns (the partials P_j, the weight-gradient blocks dW_s).
+    """
+    ns = n - s0 if ns is None else ns
+    dys = split_cols(dy, ns)
+    partials = [matmul(dys[j], transpose(col_block(w, n, s0 + j))) for j in range(ns)]
+    dws = [matmul(transpose(x), dys[j]) for j in range(ns)]
+    return partials, dws
+
+
+def row_linear_backward(x, w, dy, n: int, s0: int = 0, ns: int | None = None):
+    """Backward of the row split.
+
+    The forward output is the sum of the partials, so every shard receives the
+    whole dY, and each shard's input block keeps its own gradient (no exchange):
+        dX_s = dY W_s^T,   dW_s = X_s^T dY.
+    Returns (the input-gradient blocks dX_s, the weight-gradient blocks dW_s).
+    """
+    ns = n - s0 if ns is None else ns
+    dxs = [matmul(dy, transpose(row_block(w, n, s))) for s in range(s0, s0 + ns)]
+    dws = [matmul(transpose(x_block(x, n, s)), dy) for s in range(s0, s0 + ns)]
+    return dxs, dws
+
+
+def mlp_backward(x, w1, w2, dy, n: int, act: str = "gelu", s0: int = 0, ns: int | None = None):
+    """Backward of the Megatron MLP pair, shard by shard, float64 throughout.
+
+    With Z_s = X W1_s and H_s = act(Z_s) (recomputed here):
+        dH_s = dY W2_s^T  (the row-split layer: dY reaches every shard),
+        dZ_s = dH_s * act'(Z_s)  (elementwise, inside the shard),
+        dW2_s = H_s^T dY,  dW1_s = X^T dZ_s,
+        dX = sum_s dZ_s W1_s^T  (the column-split layer: the backward all-reduce,
+             ascending shard order).
+    Returns (dX, dW1 as the concatenation of the dW1_s, dW2 as the dW2_s stacked by rows).
+    """
+    ns = n - s0 if ns is None else ns
+    partials, dw1, dw2 = [], [], []
+    dy = widen(dy)
+    for s in range(s0, s0 + ns):
+        w1s, w2s = col_block(w1, n, s), row_block(w2, n, s)
+        z = matmul(x, w1s)
+        h = apply_act(z, act)
+        dz = matmul(dy, transpose(w2s)) * act_grad(z, act)
+        dw2.append(matmul(transpose(h), dy))
+        dw1.append(matmul(transpose(x), dz))
+        partials.append(matmul(dz, transpose(w1s)))
+    return reduce_sum(partials), concat_cols(dw1), np.vstack(dw2)
