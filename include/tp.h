@@ -97,7 +97,8 @@ typedef struct tp_matrix {
  *     Y_j = act(X W_s),  j = s - s0,
  * where W_s = W[:, s*Nout/N : (s+1)*Nout/N] and the activation is elementwise
  * on the fp32 result ([TP-topic] "Megatron-LM Tensor Parallelism": applied on
- * each shard without exchange; TP_ACT_GELU = x * Phi(x) with the exact erf).
+ * each shard without exchange; TP_ACT_GELU = x * Phi(x), Phi(x) = (1 + erf(x /
+ * sqrt 2)) / 2, evaluated in fp32 to within 5e-7 of the exact value).
  *   X  [M, K], shard_stride 0 (the same X reaches every shard).
  *   W  logical [K, Nout], N | Nout. shard_stride 0: W_s is the column slice
  *      above (ld >= Nout); > 0: W_s is the [K, Nout/N] block at
@@ -171,6 +172,72 @@ tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const 
 tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, int32_t N, int32_t s0,
                  int32_t ns, int32_t act, void* workspace, size_t* workspace_bytes, const tp_matrix* Y,
                  void* stream);
+
+/*
+ * Backward passes. The pages pair every forward collective with a backward
+ * one ([TP-topic] "Megatron-LM Tensor Parallelism": the identity operator of
+ * the forward pass becomes an all-reduce in the backward pass and vice versa;
+ * "Communication Optimization": the backward pass all-reduces gradients with
+ * the forward volume; "Memory Distribution": each shard computes the
+ * gradients of its own 1/N of the weights). Given dY, the gradient of a loss
+ * with respect to the forward output, these return the gradients with
+ * respect to X and the executed shards of W. Gradients are fp32-accumulated;
+ * dtype rules, layouts and errors are those of the forward calls. Either
+ * output descriptor may be NULL to skip that gradient (not both).
+ */
+
+/*
+ * Backward of tp_col_linear with act = NONE. X is replicated in the forward
+ * pass, so its gradient is a sum over shards (the backward all-reduce):
+ *     dX  = sum_j P_j,   P_j = dY_j W_s^T   (fp32 partials, j = s - s0)
+ *     dW_j = X^T dY_j                       (the gradient of W_s)
+ *   X, W   as in tp_col_linear.
+ *   dY     logical [M, ns*Nout/N], the layout of tp_col_linear's Y (dtype of X).
+ *   dXp    TP_F32 partials, rows = M, cols = K, P_j at ptr + j*shard_stride
+ *          (shard_stride may be 0 only when ns = 1); sum them with
+ *          tp_reduce_partials(axis = TP_SPLIT_ROWS).
+ *   dW     logical [K, ns*Nout/N], TP_F32 or TP_BF16: shard_stride 0 puts dW_j
+ *          at columns j*Nout/N; > 0 puts it at ptr + j*shard_stride.
+ */
+tp_status tp_col_linear_backward(const tp_matrix* X, const tp_matrix* W, const tp_matrix* dY, int32_t N,
+                                 int32_t s0, int32_t ns, const tp_matrix* dXp, const tp_matrix* dW,
+                                 void* stream);
+
+/*
+ * Backward of tp_row_linear. The forward output is the sum of the partials,
+ * so every shard receives the whole dY, and the gradient of each input block
+ * stays on its shard (no exchange):
+ *     dX_j = dY W_s^T,   dW_j = X_s^T dY,   j = s - s0
+ *   X, W   as in tp_row_linear.
+ *   dY     [M, Nout], dtype of X, shard_stride 0.
+ *   dX     logical [M, ns*K/N], TP_F32 or TP_BF16: shard_stride 0 puts dX_j at
+ *          columns j*K/N (the layout of X's executed blocks); > 0 at
+ *          ptr + j*shard_stride.
+ *   dW     logical [ns*K/N, Nout], TP_F32 or TP_BF16: shard_stride 0 puts dW_j
+ *          at rows j*K/N; > 0 at ptr + j*shard_stride.
+ */
+tp_status tp_row_linear_backward(const tp_matrix* X, const tp_matrix* W, const tp_matrix* dY, int32_t N,
+                                 int32_t s0, int32_t ns, const tp_matrix* dX, const tp_matrix* dW,
+                                 void* stream);
+
+/*
+ * Backward of tp_mlp. With Z_s = X W1_s and H_s = act(Z_s):
+ *     dH_s = dY W2_s^T,  dZ_s = dH_s * act'(Z_s)  (elementwise),
+ *     dW2_s = H_s^T dY,  dW1_s = X^T dZ_s,
+ *     dX = sum_s dZ_s W1_s^T                  (fp32, ascending s)
+ * H_s and Z_s are recomputed from X (they are not kept by tp_mlp). With bf16
+ * inputs Z_s, H_s and dZ_s are rounded to bf16 before they feed a product.
+ *   X, W1, W2, act, workspace, *workspace_bytes   as in tp_mlp (the workspace
+ *          holds Z, H, dZ and the partials of dX; NULL queries its size).
+ *   dY     [M, Dout], dtype of X, shard_stride 0.
+ *   dX     [M, d], TP_F32, shard_stride 0, or NULL.
+ *   dW1    logical [d, ns*F/N] as dW of tp_col_linear_backward, or NULL.
+ *   dW2    logical [ns*F/N, Dout] as dW of tp_row_linear_backward, or NULL.
+ */
+tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, const tp_matrix* dY,
+                          int32_t N, int32_t s0, int32_t ns, int32_t act, void* workspace,
+                          size_t* workspace_bytes, const tp_matrix* dX, const tp_matrix* dW1,
+                          const tp_matrix* dW2, void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* tp_status_string(int32_t status);

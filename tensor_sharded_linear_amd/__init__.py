@@ -26,6 +26,10 @@ __all__ = [
     "reduce_partials",
     "mlp",
     "mlp_workspace_bytes",
+    "col_linear_backward",
+    "row_linear_backward",
+    "mlp_backward",
+    "mlp_backward_workspace_bytes",
     "TpError",
     "library",
     "version",
@@ -209,3 +213,138 @@ def mlp(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, n: int, s0: int = 0
                           ctypes.c_void_p(_stream(x)))
     _lib.check(st, "tp_mlp")
     return out
+
+
+# ----------------------------------------------------------------------------- backward passes
+
+
+def _ref(t):
+    return ctypes.byref(t) if t is not None else None
+
+
+def _out(spec, shape3, shape2, partitioned, dtype, device):
+    """An output tensor: the one given, a new one (spec True), or None (spec False/None)."""
+    if spec is None or spec is False:
+        return None
+    if isinstance(spec, torch.Tensor):
+        return spec
+    return torch.empty(shape3 if partitioned else shape2, dtype=dtype, device=device)
+
+
+def col_linear_backward(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, n: int, s0: int = 0,
+                        ns: int | None = None, dx_partials=True, dw=True, dw_dtype: torch.dtype = torch.float32,
+                        partitioned_dw: bool = False):
+    """Backward of col_linear (no activation): returns (P, dW).
+
+    dy: [M, ns*Nout/n] or partitioned [ns, M, Nout/n].
+    P: fp32 [ns, M, K] with P_j = dY_j W_{s0+j}^T; dX is their sum (reduce_partials).
+    dW: [K, ns*Nout/n] (or [ns, K, Nout/n] if partitioned_dw) with dW_j = X^T dY_j.
+    Pass False to skip an output or a tensor to write into.
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(x, w, dy)
+    _check_stack(w, s0, ns)
+    m, k = x.shape
+    nout = w.shape[1] if w.dim() == 2 else n * w.shape[2]
+    width = nout // n if n > 0 else 0
+    p = _out(dx_partials, (ns, m, k), None, True, torch.float32, x.device)
+    g = _out(dw, (ns, k, width), (k, ns * width), partitioned_dw, dw_dtype, x.device)
+    pm = None if p is None else _lib.matrix(p.data_ptr(), TP_F32, m, k, max(p.stride(1), k),
+                                            p.stride(0) if p.shape[0] > 1 else 0)
+    gm = None if g is None else _blocks(g, k, ns * width)
+    st = library().tp_col_linear_backward(ctypes.byref(_full(x)), ctypes.byref(_blocks(w, k, nout)),
+                                          ctypes.byref(_blocks(dy, m, ns * width)), n, s0, ns, _ref(pm), _ref(gm),
+                                          ctypes.c_void_p(_stream(x)))
+    _lib.check(st, "tp_col_linear_backward")
+    return p, g
+
+
+def row_linear_backward(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, n: int, s0: int = 0,
+                        ns: int | None = None, dx=True, dw=True, dx_dtype: torch.dtype = torch.float32,
+                        dw_dtype: torch.dtype = torch.float32, partitioned: bool = False):
+    """Backward of row_linear: returns (dX, dW) for the executed shards.
+
+    dX: [M, ns*K/n] (or [ns, M, K/n] if partitioned) with dX_j = dY W_{s0+j}^T.
+    dW: [ns*K/n, Nout] (or [ns, K/n, Nout] if partitioned) with dW_j = X_{s0+j}^T dY.
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(x, w, dy)
+    _check_stack(x, s0, ns)
+    _check_stack(w, s0, ns)
+    m = x.shape[0] if x.dim() == 2 else x.shape[1]
+    k = x.shape[1] if x.dim() == 2 else n * x.shape[2]
+    nout = w.shape[1] if w.dim() == 2 else w.shape[2]
+    kb = k // n if n > 0 else 0
+    a = _out(dx, (ns, m, kb), (m, ns * kb), partitioned, dx_dtype, x.device)
+    g = _out(dw, (ns, kb, nout), (ns * kb, nout), partitioned, dw_dtype, x.device)
+    am = None if a is None else _blocks(a, m, ns * kb)
+    gm = None if g is None else _blocks(g, ns * kb, nout)
+    st = library().tp_row_linear_backward(ctypes.byref(_blocks(x, m, k)), ctypes.byref(_blocks(w, k, nout)),
+                                          ctypes.byref(_full(dy)), n, s0, ns, _ref(am), _ref(gm),
+                                          ctypes.c_void_p(_stream(x)))
+    _lib.check(st, "tp_row_linear_backward")
+    return a, g
+
+
+def _mlp_bwd_mats(x, w1, w2, dy, n, ns, dx, dw1, dw2):
+    xm, w1m, w2m, dout = _mlp_mats(x, w1, w2, n)
+    m, d = x.shape
+    f = w1.shape[1] if w1.dim() == 2 else n * w1.shape[2]
+    width = f // n if n > 0 else 0
+    am = None if dx is None else _full(dx)
+    g1 = None if dw1 is None else _blocks(dw1, d, ns * width)
+    g2 = None if dw2 is None else _blocks(dw2, ns * width, dout)
+    return xm, w1m, w2m, _full(dy), am, g1, g2
+
+
+def mlp_backward_workspace_bytes(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, dy: torch.Tensor, n: int,
+                                 s0: int = 0, ns: int | None = None, act: str = "gelu", dx: bool = True,
+                                 dw1: bool = True, dw2: bool = True) -> int:
+    """Device scratch that mlp_backward() needs for these operands and requested gradients."""
+    ns = n - s0 if ns is None else ns
+    _check_stack(w1, s0, ns)
+    _check_stack(w2, s0, ns)
+    m, d = x.shape
+    f = w1.shape[1] if w1.dim() == 2 else n * w1.shape[2]
+    dout = w2.shape[1] if w2.dim() == 2 else w2.shape[2]
+    width = f // n if n > 0 else 0
+    xm, w1m, w2m, dout = _mlp_mats(x, w1, w2, n)
+    am = _lib.matrix(0, TP_F32, m, d, d, 0) if dx else None
+    g1 = _lib.matrix(0, TP_F32, d, ns * width, ns * width, 0) if dw1 else None
+    g2 = _lib.matrix(0, TP_F32, ns * width, dout, dout, 0) if dw2 else None
+    size = ctypes.c_size_t(0)
+    st = library().tp_mlp_backward(ctypes.byref(xm), ctypes.byref(w1m), ctypes.byref(w2m), ctypes.byref(_full(dy)),
+                                   n, s0, ns, _ACTS[act], None, ctypes.byref(size), _ref(am), _ref(g1), _ref(g2),
+                                   None)
+    _lib.check(st, "tp_mlp_backward(workspace query)")
+    return int(size.value)
+
+
+def mlp_backward(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, dy: torch.Tensor, n: int, s0: int = 0,
+                 ns: int | None = None, act: str = "gelu", dx=True, dw1=True, dw2=True,
+                 dw_dtype: torch.dtype = torch.float32, workspace: torch.Tensor | None = None):
+    """Backward of mlp(): returns (dX fp32 [M, d], dW1 [d, ns*F/n], dW2 [ns*F/n, Dout]).
+
+    Pass False to skip a gradient or a tensor to write into (dW1/dW2 may be
+    shard-major stacks [ns, d, F/n] / [ns, F/n, Dout]).
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(x, w1, w2, dy)
+    m, d = x.shape
+    f = w1.shape[1] if w1.dim() == 2 else n * w1.shape[2]
+    dout = w2.shape[1] if w2.dim() == 2 else w2.shape[2]
+    width = f // n if n > 0 else 0
+    a = _out(dx, None, (m, d), False, torch.float32, x.device)
+    g1 = _out(dw1, None, (d, ns * width), False, dw_dtype, x.device)
+    g2 = _out(dw2, None, (ns * width, dout), False, dw_dtype, x.device)
+    need = mlp_backward_workspace_bytes(x, w1, w2, dy, n, s0, ns, act, a is not None, g1 is not None,
+                                        g2 is not None)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    xm, w1m, w2m, dym, am, g1m, g2m = _mlp_bwd_mats(x, w1, w2, dy, n, ns, a, g1, g2)
+    size = ctypes.c_size_t(workspace.numel())
+    st = library().tp_mlp_backward(ctypes.byref(xm), ctypes.byref(w1m), ctypes.byref(w2m), ctypes.byref(dym), n,
+                                   s0, ns, _ACTS[act], ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(size),
+                                   _ref(am), _ref(g1m), _ref(g2m), ctypes.c_void_p(_stream(x)))
+    _lib.check(st, "tp_mlp_backward")
+    return a, g1, g2

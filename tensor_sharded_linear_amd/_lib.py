@@ -35,6 +35,9 @@ EXPORTS = (
     "tp_row_linear",
     "tp_reduce_partials",
     "tp_mlp",
+    "tp_col_linear_backward",
+    "tp_row_linear_backward",
+    "tp_mlp_backward",
     "tp_status_string",
     "tp_version",
 )
@@ -85,6 +88,15 @@ def load() -> ctypes.CDLL:
     lib.tp_mlp.argtypes = [_M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), _M, ctypes.c_void_p]
     lib.tp_mlp.restype = ctypes.c_int32
+    lib.tp_col_linear_backward.argtypes = [_M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _M, _M,
+                                           ctypes.c_void_p]
+    lib.tp_col_linear_backward.restype = ctypes.c_int32
+    lib.tp_row_linear_backward.argtypes = [_M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _M, _M,
+                                           ctypes.c_void_p]
+    lib.tp_row_linear_backward.restype = ctypes.c_int32
+    lib.tp_mlp_backward.argtypes = [_M, _M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), _M, _M, _M, ctypes.c_void_p]
+    lib.tp_mlp_backward.restype = ctypes.c_int32
     lib.tp_status_string.argtypes = [ctypes.c_int32]
     lib.tp_status_string.restype = ctypes.c_char_p
     lib.tp_version.argtypes = []

@@ -1,5 +1,6 @@
 // Element-guarded GEMM for any dtype (fp32 or bf16 inputs), alignment and shape:
-// C_z = act(A_z B_z) with fp32 multiply-add in ascending k for every output.
+// C_z = act(op(A_z) op(B_z)) with fp32 multiply-add in ascending k for every
+// output; either operand may be stored transposed.
 //
 // It serves the exact fp32 path (integer-valued inputs give exact results, as
 // in the worked example of the "Tensor Parallelism" entry of the AI Glossary,
@@ -39,10 +40,12 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d, int tiles
       const int e = tid + 256 * i;
       const int r = e / TK, kk = e % TK;  // A tile: 64 rows x 16 k
       const int64_t gm = m0 + r, gk = k0 + kk;
-      As[kk][r] = (gm < d.M && gk < d.K) ? ld_elem<T>(d.A, abase + gm * d.lda + gk) : 0.f;
+      const int64_t ai = d.a_trans ? gk * d.lda + gm : gm * d.lda + gk;
+      As[kk][r] = (gm < d.M && gk < d.K) ? ld_elem<T>(d.A, abase + ai) : 0.f;
       const int kb = e / TN, c = e % TN;  // B tile: 16 k x 64 columns
       const int64_t gkb = k0 + kb, gn = n0 + c;
-      Bs[kb][c] = (gkb < d.K && gn < d.N) ? ld_elem<T>(d.B, bbase + gkb * d.ldb + gn) : 0.f;
+      const int64_t bi = d.b_trans ? gn * d.ldb + gkb : gkb * d.ldb + gn;
+      Bs[kb][c] = (gkb < d.K && gn < d.N) ? ld_elem<T>(d.B, bbase + bi) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -67,7 +70,10 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d, int tiles
       const int64_t gn = n0 + tx + 16 * j;
       if (gm < d.M && gn < d.N) {
         float v = acc[i][j];
-        if (ACT == ACT_GELU) v = gelu(v);
+        const int64_t xo = z * d.sX + gm * d.ldx + gn;  // the side matrix has the input dtype
+        if (ACT == ACT_GELU_SAVE) static_cast<T*>(d.aux)[xo] = (T)v;
+        if (ACT == ACT_GELU || ACT == ACT_GELU_SAVE) v = gelu(v);
+        if (ACT == ACT_DGELU) v *= gelu_grad((float)static_cast<const T*>(d.aux)[xo]);
         const int64_t off = z * d.sC + gm * d.ldc + gn;
         if (OUT == OUT_F32) static_cast<float*>(d.C)[off] = v;
         else static_cast<__bf16*>(d.C)[off] = (__bf16)v;
@@ -76,17 +82,23 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmDesc d, int tiles
   }
 }
 
-template <typename T>
-hipError_t launch_typed(const GemmDesc& d, dim3 grid, int tiles_n, hipStream_t s) {
+template <typename T, int OUT>
+hipError_t launch_act(const GemmDesc& d, dim3 grid, int tiles_n, hipStream_t s) {
   const dim3 block(256);
-  if (d.out_kind == OUT_F32) {
-    if (d.act == ACT_GELU) gemm_generic_kernel<T, OUT_F32, ACT_GELU><<<grid, block, 0, s>>>(d, tiles_n);
-    else gemm_generic_kernel<T, OUT_F32, ACT_NONE><<<grid, block, 0, s>>>(d, tiles_n);
-  } else {
-    if (d.act == ACT_GELU) gemm_generic_kernel<T, OUT_BF16, ACT_GELU><<<grid, block, 0, s>>>(d, tiles_n);
-    else gemm_generic_kernel<T, OUT_BF16, ACT_NONE><<<grid, block, 0, s>>>(d, tiles_n);
+  switch (d.act) {
+    case ACT_NONE: gemm_generic_kernel<T, OUT, ACT_NONE><<<grid, block, 0, s>>>(d, tiles_n); break;
+    case ACT_GELU: gemm_generic_kernel<T, OUT, ACT_GELU><<<grid, block, 0, s>>>(d, tiles_n); break;
+    case ACT_GELU_SAVE: gemm_generic_kernel<T, OUT, ACT_GELU_SAVE><<<grid, block, 0, s>>>(d, tiles_n); break;
+    case ACT_DGELU: gemm_generic_kernel<T, OUT, ACT_DGELU><<<grid, block, 0, s>>>(d, tiles_n); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_typed(const GemmDesc& d, dim3 grid, int tiles_n, hipStream_t s) {
+  return d.out_kind == OUT_F32 ? launch_act<T, OUT_F32>(d, grid, tiles_n, s)
+                               : launch_act<T, OUT_BF16>(d, grid, tiles_n, s);
 }
 
 }  // namespace

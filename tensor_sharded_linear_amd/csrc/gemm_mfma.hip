@@ -1,22 +1,29 @@
-// Large-tile bf16 GEMM on the gfx950 matrix cores: C_z = act(A_z B_z), fp32 accumulate.
+// Large-tile bf16 GEMM on the gfx950 matrix cores: C_z = act(op(A_z) op(B_z)),
+// fp32 accumulate.
 //
 // This is the per-shard dense product of the sharded linear layer ("Tensor
 // Parallelism" topic page, chipfoundryservices.com, sections "Column-Wise
 // Parallelism" and "Row-Wise Parallelism": each shard multiplies its input by
 // its block of W). All shards of one call form one launch: either one wide
 // product (column shards stored side by side) or a batch indexed by shard.
+// The same kernel serves the backward products of those layers (section
+// "Megatron-LM Tensor Parallelism", identity operators whose backward is the
+// all-reduce): dX = dY W^T takes B transposed, dW = X^T dY takes A transposed.
 //
 // Tile 256 x 256 x 64, 512 threads = 8 waves in a 2 x 4 grid (two waves per
 // SIMD); each wave owns a 128 x 64 block of C held as 4 x 2
 // v_mfma_f32_32x32x16_bf16 accumulators.
-// A (row-major, K contiguous) and B (row-major, N contiguous: the pages'
-// [in, out] weight) go from HBM straight into LDS with buffer loads in LDS
-// mode (no register staging), two stages deep. A fragments are read with
-// ds_read_b128; B fragments need K-contiguous lanes, which gfx950 provides
-// with the LDS transpose read ds_read_b64_tr_b16. The fragments of the next
-// 16-wide k step are read while the matrix cores work on the current one.
-// Rows past M or K, and K chunks past K, read as zero through the buffer
-// range check.
+// Each operand tile goes from HBM straight into LDS with buffer loads in LDS
+// mode (no register staging), two stages deep, in one of two layouts chosen by
+// how the operand is stored:
+//   K-rows: 256 rows (of M or N) x 64 k, 128-byte rows (A as [M, K], B as
+//     [N, K]); fragments are read with ds_read_b128.
+//   MN-rows: 64 k-rows x 256 (of M or N), 512-byte rows (A as [K, M], B as
+//     [K, N], the pages' [in, out] weight); fragments need K-contiguous lanes,
+//     which gfx950 provides with the LDS transpose read ds_read_b64_tr_b16.
+// The fragments of the next 16-wide k step are read while the matrix cores
+// work on the current one. Rows past M, N or K and k chunks past K read as
+// zero through the buffer range check.
 #include "tp_internal.h"
 
 namespace tp {
@@ -25,16 +32,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 #define TP_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512, NWAVES = NTHREADS / 64;
+constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512;
 constexpr int WM = 128, WN = 64;          // wave tile
 constexpr int FM = WM / 32, FN = WN / 32;  // 32 x 32 fragments per wave
-constexpr int A_BYTES = BM * BK * 2;  // one LDS stage of A: 32 KB
-constexpr int B_BYTES = BK * BN * 2;  // one LDS stage of B: 32 KB
+constexpr int TILE_BYTES = 256 * BK * 2;   // one LDS stage of one operand: 32 KB
 constexpr int GROUP_M = 4;  // tile rows per group: 32 resident tiles form a 4 x 8 block per XCD
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every range used here
@@ -68,18 +72,108 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // XOR swizzles of 16-byte chunks that keep the fragment reads free of bank
-// conflicts: A rows hold 64 elements (8 chunks), B rows 256 elements (32 chunks).
-__device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int swz_b(int krow) { return ((krow & 1) * 6) ^ (((krow >> 1) & 1) * 12); }
+// conflicts: K-rows tiles hold 8 chunks per row, MN-rows tiles 32.
+__device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz_mn(int krow) { return ((krow & 1) * 6) ^ (((krow >> 1) & 1) * 12); }
 
-template <int OUT, int ACT>
+// One operand of the product: where its tile comes from and how it is laid out.
+// KROWS: the operand is stored with k contiguous (A [M, K] or B [N, K]).
+template <bool KROWS>
+struct Operand {
+  const __bf16* tile;  // element (row/col origin of the tile, k = 0) of this batch entry
+  int64_t ld;          // row stride of the stored matrix, elements
+  int extent;          // rows (KROWS) or columns (MN-rows) of the tile inside the matrix
+  uint32_t voff, srow;
+  int kc;              // KROWS: the k chunk this lane loads
+
+  __device__ __forceinline__ void init(int lane, int wave) {
+    if (KROWS) {
+      // region r (1 KB) = rows 8r .. 8r+7; lane l -> row + (l >> 3), slot l & 7,
+      // k-chunk (l & 7) ^ swz_k(row) = (l & 7) ^ (l >> 3) ^ w for regions w + 8 i
+      kc = (lane & 7) ^ (lane >> 3) ^ wave;
+      voff = (uint32_t)((lane >> 3) * ld * 2 + kc * 16);
+      srow = (uint32_t)(8 * ld * 2);
+    } else {
+      // region r = k-rows 2r, 2r+1; lane l -> k-row + (l >> 5), slot l & 31,
+      // chunk (l & 31) ^ swz_mn(k-row), the same for regions w + 8 i
+      kc = 0;
+      voff = (uint32_t)((lane >> 5) * ld * 2 + (((lane & 31) ^ swz_mn(2 * wave + (lane >> 5))) * 16));
+      srow = (uint32_t)(2 * ld * 2);
+    }
+  }
+
+  // LDS-mode loads of k-tile [k0, k0 + 64) into one stage: wave w fills regions
+  // w + 8 i (i = 0..3), one instruction each; lane l lands at region + 16 l.
+  __device__ __forceinline__ void load(int k0, int krem, char* stage, int wave) const {
+    char* base = stage + wave * 1024;
+    if (KROWS) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(tile + k0, ((int64_t)(extent - 1) * ld + krem) * 2);
+      const uint32_t o = kc * 8 < krem ? voff : kOOB;  // k chunks at or past K read as zero
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TP_LDS(base + i * 8192), 16, o, (wave + 8 * i) * srow, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(tile + (int64_t)k0 * ld, ((int64_t)(min(krem, BK) - 1) * ld + extent) * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TP_LDS(base + i * 8192), 16, voff, (wave + 8 * i) * srow, 0, 0);
+    }
+  }
+};
+
+// Fragment reads of F 32-wide blocks starting at row/col `pos` of the tile.
+// Either layout yields the lane format both MFMA operands use: lane l holds
+// row/col (l & 31) of the block and k values 8 (l >> 5) .. + 7 of the k step.
+template <bool KROWS, int F>
+struct Frags {
+  int off[F];
+  int sw;
+  __device__ __forceinline__ void init(int lane, int pos) {
+    if (KROWS) {
+      // rows of block f differ from row pos + (lane & 31) by 32 f: swz_k changes by (4 f) & 7
+#pragma unroll
+      for (int f = 0; f < F; ++f) off[f] = (pos + f * 32 + (lane & 31)) * 128;
+      sw = swz_k(pos + (lane & 31));
+    } else {
+      // transpose reads: lane (G = lane >> 4, j = lane & 15) supplies k-row
+      // 8 (G >> 1) + 4 t + (j >> 2) and columns 16 (G & 1) + 4 (j & 3) .. + 3 of a
+      // 32-wide block, and receives 4 k values of column 16 (G & 1) + j
+      const int G = lane >> 4, j16 = lane & 15;
+      const int kr = 8 * (G >> 1) + (j16 >> 2);
+      sw = swz_mn(kr);  // k-rows used with this lane differ by multiples of 4
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int col = pos + f * 32 + 16 * (G & 1) + 4 * (j16 & 3);
+        off[f] = kr * 512 + (((col >> 3) ^ sw) << 4) + (col & 4) * 2;
+      }
+    }
+  }
+  __device__ __forceinline__ void read(const char* stage, int kk, int lane, bf16x8 (&out)[F]) const {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      if (KROWS) {
+        const int kc = kk * 2 + (lane >> 5);
+        out[f] = *reinterpret_cast<const bf16x8*>(stage + off[f] + ((kc ^ sw ^ ((4 * f) & 7)) << 4));
+      } else {
+        const char* p = stage + off[f] + kk * 16 * 512;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4 * 512));
+        out[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+  }
+};
+
+template <int OUT, int ACT, bool AT, bool BT>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
   // Two stages of A and B, each its own array so the compiler can tell the
   // stage being filled by LDS-mode loads from the stage being read.
-  __shared__ __attribute__((aligned(1024))) char sA0[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sA1[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB0[B_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB1[B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sA0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sA1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB1[TILE_BYTES];
+  constexpr bool A_KROWS = !AT, B_KROWS = BT;
 
   const GemmDesc& d = p.d;
   const int logical = xcd_remap(blockIdx.x, p.total);
@@ -102,91 +196,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t M = d.M, N = d.N, K = d.K;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t lda = d.lda, ldb = d.ldb;
   const int rows_here = (int)min<int64_t>(M - m0, BM);
+  const int cols_here = (int)min<int64_t>(N - n0, BN);
 
-  const __bf16* Az = static_cast<const __bf16*>(d.A) + z * d.sA + m0 * lda;
-  const __bf16* Bz = static_cast<const __bf16*>(d.B) + z * d.sB + n0;
-
-  // LDS-mode loads: a stage of A (or B) is 32 regions of 1 KB; wave w fills
-  // regions w + 8 i (i = 0..3) with one instruction each, and lane l lands at
-  // region + 16 l, so each lane fetches the global chunk that the swizzle
-  // places in that slot.
-  //   A region r: rows 8r .. 8r+7; lane l -> row + (l >> 3), slot l & 7,
-  //     k-chunk (l & 7) ^ swz_a(row) = (l & 7) ^ (l >> 3) ^ w, the same for every i.
-  //   B region r: k-rows 2r, 2r+1; lane l -> k-row + (l >> 5), slot l & 31,
-  //     n-chunk (l & 31) ^ swz_b(k-row), the same for every i.
-  // The lane-dependent part of each offset goes in the vector offset, the
-  // uniform row part in the scalar offset.
-  const int a_kc = (lane & 7) ^ (lane >> 3) ^ wave;
-  const uint32_t a_voff = (uint32_t)((lane >> 3) * lda * 2 + a_kc * 16);
-  const uint32_t a_srow = (uint32_t)(8 * lda * 2);   // bytes per region (8 rows) of A
-  const int b_rb = 2 * wave + (lane >> 5);
-  const uint32_t b_voff = (uint32_t)((lane >> 5) * ldb * 2 + (((lane & 31) ^ swz_b(b_rb)) * 16));
-  const uint32_t b_srow = (uint32_t)(2 * ldb * 2);   // bytes per region (2 k-rows) of B
+  Operand<A_KROWS> opa;
+  Operand<B_KROWS> opb;
+  opa.ld = d.lda;
+  opb.ld = d.ldb;
+  const __bf16* Az = static_cast<const __bf16*>(d.A) + z * d.sA;
+  const __bf16* Bz = static_cast<const __bf16*>(d.B) + z * d.sB;
+  // K-rows tiles start at row m0 (n0); MN-rows tiles at column m0 (n0) of k-row 0.
+  opa.tile = A_KROWS ? Az + m0 * d.lda : Az + m0;
+  opb.tile = B_KROWS ? Bz + n0 * d.ldb : Bz + n0;
+  // MN-rows extents run to the end of the row, so the columns past M (N) of a
+  // partial tile read the next row's values; they only reach rows (columns) of
+  // C that the epilogue drops.
+  opa.extent = A_KROWS ? rows_here : (int)(M - m0);
+  opb.extent = B_KROWS ? cols_here : (int)(N - n0);
+  opa.init(lane, wave);
+  opb.init(lane, wave);
 
   const int K32 = (int)K;
   const int KT = (K32 + BK - 1) / BK;
-
   auto issue_loads = [&](int kt, char* sa, char* sb) {
     const int k0 = kt * BK;
-    const int krem = K32 - k0;
-    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Az + k0, ((int64_t)(rows_here - 1) * lda + krem) * 2);
-    const __amdgpu_buffer_rsrc_t brsrc =
-        make_rsrc(Bz + (int64_t)k0 * ldb, ((int64_t)(min(krem, BK) - 1) * ldb + (N - n0)) * 2);
-    char* abase = sa + wave * 1024;
-    char* bbase = sb + wave * 1024;
-    // k-chunks at or past K read as zero through an out-of-range offset
-    const uint32_t ao = a_kc * 8 < krem ? a_voff : kOOB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, TP_LDS(abase + i * 8192), 16, ao,
-                                               (wave + 8 * i) * a_srow, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, TP_LDS(bbase + i * 8192), 16, b_voff,
-                                               (wave + 8 * i) * b_srow, 0, 0);
+    opa.load(k0, K32 - k0, sa, wave);
+    opb.load(k0, K32 - k0, sb, wave);
   };
 
-  // Fragment addressing.
-  // A fragment (32 rows x 16 k): lane holds row (lane & 31), k-chunk 2 kk + (lane >> 5).
-  // B fragment via transpose reads: lane (G = lane >> 4, j = lane & 15) supplies
-  // k-row 8 (G >> 1) + 4 t + (j >> 2) and columns 16 (G & 1) + 4 (j & 3) .. + 3
-  // of a 32-column block; it receives 4 k-values of column 16 (G & 1) + j.
-  int a_off[FM];
-#pragma unroll
-  for (int im = 0; im < FM; ++im) {
-    const int row = wm * WM + im * 32 + (lane & 31);
-    a_off[im] = row * 128;
-  }
-  const int a_h = lane >> 5;
-  const int a_sw0 = swz_a(wm * WM + (lane & 31));  // rows differ by multiples of 32 below
-  const int G = lane >> 4, j16 = lane & 15;
-  const int b_kr = 8 * (G >> 1) + (j16 >> 2);
-  const int b_sw = swz_b(b_kr);  // k-rows used with this lane differ by multiples of 4
-  int b_off[FN];
-#pragma unroll
-  for (int jn = 0; jn < FN; ++jn) {
-    const int col = wn * WN + jn * 32 + 16 * (G & 1) + 4 * (j16 & 3);
-    b_off[jn] = b_kr * 512 + ((((col >> 3) ^ b_sw)) << 4) + (col & 4) * 2;
-  }
-
+  Frags<A_KROWS, FM> ra;
+  Frags<B_KROWS, FN> rb;
+  ra.init(lane, wm * WM);
+  rb.init(lane, wn * WN);
   bf16x8 fa[2][FM], fb[2][FN];
   auto read_frags = [&](const char* a, const char* b, int kk, int slot) {
-#pragma unroll
-    for (int im = 0; im < FM; ++im) {
-      // rows of fragment im differ from row (wm*128 + lane&31) by 32 im: swz_a changes by (4 im) & 7
-      const int sw = a_sw0 ^ ((4 * im) & 7);
-      const int kc = kk * 2 + a_h;
-      fa[slot][im] = *reinterpret_cast<const bf16x8*>(a + a_off[im] + ((kc ^ sw) << 4));
-    }
-#pragma unroll
-    for (int jn = 0; jn < FN; ++jn) {
-      const char* bp = b + b_off[jn] + kk * 16 * 512;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(bp));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(bp + 4 * 512));
-      fb[slot][jn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    ra.read(a, kk, lane, fa[slot]);
+    rb.read(b, kk, lane, fb[slot]);
   };
 
   f32x16 acc[FM][FN];
@@ -229,25 +274,48 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
   // column l % 32 of its 32 x 32 block. Stores go through a buffer resource
   // over this tile's rows of C: rows past M fall outside it and are dropped;
   // columns past N are masked per lane. The row part of every offset is
-  // uniform and travels in the scalar offset.
+  // uniform and travels in the scalar offset. The bf16 side matrix (the saved
+  // pre-activation, or the one the GeLU derivative is taken of) has the same
+  // shape and is addressed the same way.
   const int64_t ldc = d.ldc;
   constexpr int ES = OUT == OUT_F32 ? 4 : 2;
   char* Ct = static_cast<char*>(d.C) + (z * d.sC + m0 * ldc + n0) * ES;
   const __amdgpu_buffer_rsrc_t crsrc = make_rsrc(Ct, ((int64_t)(rows_here - 1) * ldc + (N - n0)) * ES);
   const uint32_t row_bytes = (uint32_t)(ldc * ES);
+  constexpr bool HAS_AUX = ACT == ACT_GELU_SAVE || ACT == ACT_DGELU;
+  __amdgpu_buffer_rsrc_t xrsrc = crsrc;
+  uint32_t xrow_bytes = 0;
+  if (HAS_AUX) {
+    char* Xt = static_cast<char*>(d.aux) + (z * d.sX + m0 * d.ldx + n0) * 2;
+    xrsrc = make_rsrc(Xt, ((int64_t)(rows_here - 1) * d.ldx + (N - n0)) * 2);
+    xrow_bytes = (uint32_t)(d.ldx * 2);
+  }
 #pragma unroll
   for (int im = 0; im < FM; ++im) {
 #pragma unroll
     for (int jn = 0; jn < FN; ++jn) {
       const int col = wn * WN + jn * 32 + (lane & 31);
       const int row0 = wm * WM + im * 32 + 4 * (lane >> 5);
-      const uint32_t voff = (n0 + col < N) ? (uint32_t)(row0 * row_bytes + col * ES) : kOOB;
+      const bool in = n0 + col < N;
+      const uint32_t voff = in ? (uint32_t)(row0 * row_bytes + col * ES) : kOOB;
+      const uint32_t xoff = in ? (uint32_t)(row0 * xrow_bytes + col * 2) : kOOB;
+      unsigned short zb[16];
+      if (ACT == ACT_DGELU) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          zb[e] = __builtin_amdgcn_raw_buffer_load_b16(xrsrc, xoff, (uint32_t)(8 * (e >> 2) + (e & 3)) * xrow_bytes, 0);
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float v = acc[im][jn][e];
-        if (ACT == ACT_GELU) v = gelu(v);
-        const uint32_t srow = (uint32_t)(8 * (e >> 2) + (e & 3)) * row_bytes;
-        if (OUT == OUT_F32)  // fp32 partials are streamed out (nontemporal): measured 12-15% faster
+        const int erow = 8 * (e >> 2) + (e & 3);
+        if (ACT == ACT_GELU_SAVE)
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), xrsrc, xoff,
+                                                (uint32_t)erow * xrow_bytes, 0);
+        if (ACT == ACT_GELU || ACT == ACT_GELU_SAVE) v = gelu(v);
+        if (ACT == ACT_DGELU) v *= gelu_grad((float)__builtin_bit_cast(__bf16, zb[e]));
+        const uint32_t srow = (uint32_t)erow * row_bytes;
+        if (OUT == OUT_F32)  // fp32 results (partials) are streamed out (nontemporal): measured 6-15% faster
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), crsrc, voff, srow, kStoreNT);
         else
           __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), crsrc, voff, srow, 0);
@@ -256,16 +324,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
   }
 }
 
+template <int OUT, int ACT, bool AT, bool BT>
+void launch_one(const Params& p, hipStream_t s) {
+  gemm_bf16_mfma_kernel<OUT, ACT, AT, BT><<<dim3((unsigned)p.total), dim3(NTHREADS), 0, s>>>(p);
+}
+
 }  // namespace
 
 bool gemm_mfma_supported(const GemmDesc& d) {
   if (!d.in_bf16) return false;
-  if ((d.K & 7) || (d.N & 7) || (d.lda & 7) || (d.ldb & 7) || (d.sA & 7) || (d.sB & 7)) return false;
+  if ((d.N & 7) || (d.lda & 7) || (d.ldb & 7) || (d.sA & 7) || (d.sB & 7)) return false;
+  // K-rows tiles load k in chunks of 8 (their k tail is masked per chunk);
+  // MN-rows tiles load along M or N in chunks of 8 (their k tail is masked per row)
+  const bool krows = !d.a_trans || d.b_trans;
+  if (krows && (d.K & 7)) return false;
+  if (d.a_trans && (d.M & 7)) return false;
   if ((reinterpret_cast<uintptr_t>(d.A) & 15) || (reinterpret_cast<uintptr_t>(d.B) & 15)) return false;
-  // 31-bit in-tile offsets: 256 rows of A and 64 rows of B from the tile origin.
-  if ((int64_t)BM * d.lda * 2 >= (1ll << 31) || (int64_t)BK * d.ldb * 2 >= (1ll << 31)) return false;
-  // and 256 rows of C
+  // 31-bit in-tile offsets: 256 rows of a K-rows tile and 64 k-rows of an MN-rows tile from the tile origin.
+  const int64_t a_rows = d.a_trans ? BK : BM, b_rows = d.b_trans ? BN : BK;
+  if (a_rows * d.lda * 2 >= (1ll << 31) || b_rows * d.ldb * 2 >= (1ll << 31)) return false;
+  // and 256 rows of C (and of the side matrix)
   if ((int64_t)BM * d.ldc * (d.out_kind == OUT_F32 ? 4 : 2) >= (1ll << 31)) return false;
+  if ((d.act == ACT_GELU_SAVE || d.act == ACT_DGELU) && (int64_t)BM * d.ldx * 2 >= (1ll << 31)) return false;
   return true;
 }
 
@@ -278,13 +358,39 @@ hipError_t launch_gemm_mfma(const GemmDesc& d, hipStream_t stream) {
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
   p.total = (int)total;
-  dim3 grid((unsigned)total), block(NTHREADS);
-  if (d.out_kind == OUT_F32) {
-    if (d.act == ACT_GELU) gemm_bf16_mfma_kernel<OUT_F32, ACT_GELU><<<grid, block, 0, stream>>>(p);
-    else gemm_bf16_mfma_kernel<OUT_F32, ACT_NONE><<<grid, block, 0, stream>>>(p);
+  const bool f32 = d.out_kind == OUT_F32;
+  if (!d.a_trans && !d.b_trans) {
+    // forward products
+    if (d.act == ACT_GELU_SAVE) {
+      if (f32) return hipErrorInvalidValue;
+      launch_one<OUT_BF16, ACT_GELU_SAVE, false, false>(p, stream);
+    } else if (d.act == ACT_GELU) {
+      if (f32) launch_one<OUT_F32, ACT_GELU, false, false>(p, stream);
+      else launch_one<OUT_BF16, ACT_GELU, false, false>(p, stream);
+    } else if (d.act == ACT_NONE) {
+      if (f32) launch_one<OUT_F32, ACT_NONE, false, false>(p, stream);
+      else launch_one<OUT_BF16, ACT_NONE, false, false>(p, stream);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (!d.a_trans && d.b_trans) {
+    // dX = dY W^T, optionally times GeLU'(pre-activation)
+    if (d.act == ACT_DGELU) {
+      if (f32) launch_one<OUT_F32, ACT_DGELU, false, true>(p, stream);
+      else launch_one<OUT_BF16, ACT_DGELU, false, true>(p, stream);
+    } else if (d.act == ACT_NONE) {
+      if (f32) launch_one<OUT_F32, ACT_NONE, false, true>(p, stream);
+      else launch_one<OUT_BF16, ACT_NONE, false, true>(p, stream);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (d.a_trans && !d.b_trans) {
+    // dW = X^T dY
+    if (d.act != ACT_NONE) return hipErrorInvalidValue;
+    if (f32) launch_one<OUT_F32, ACT_NONE, true, false>(p, stream);
+    else launch_one<OUT_BF16, ACT_NONE, true, false>(p, stream);
   } else {
-    if (d.act == ACT_GELU) gemm_bf16_mfma_kernel<OUT_BF16, ACT_GELU><<<grid, block, 0, stream>>>(p);
-    else gemm_bf16_mfma_kernel<OUT_BF16, ACT_NONE><<<grid, block, 0, stream>>>(p);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -249,6 +249,7 @@ int64_t chunk_for(int64_t K, int ksplit) {
 
 bool gemm_skinny_supported(const GemmDesc& d) {
   if (!d.in_bf16 || d.M < 1 || d.M > kSkinnyMaxRows) return false;
+  if (d.a_trans || d.b_trans || (d.act != ACT_NONE && d.act != ACT_GELU)) return false;
   if ((d.K & 7) || (d.N & 7) || (d.lda & 7) || (d.ldb & 7) || (d.sA & 7) || (d.sB & 7)) return false;
   if ((reinterpret_cast<uintptr_t>(d.A) & 15) || (reinterpret_cast<uintptr_t>(d.B) & 15)) return false;
   if ((int64_t)SBK * d.ldb * 2 >= (1ll << 31)) return false;

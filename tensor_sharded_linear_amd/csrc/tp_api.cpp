@@ -197,6 +197,82 @@ tp_status plan_row(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// ns consecutive blocks of one tp_matrix: block j starts `step` elements after
+// block j-1 (a column or row slice of one matrix when shard_stride is 0,
+// shard-major blocks otherwise), the first at block index `first`.
+struct Blocks {
+  const char* base;
+  int64_t ld, step;
+  int32_t dtype;
+};
+
+Blocks col_blocks(const tp_matrix* m, int64_t first, int64_t bcols) {
+  Blocks b;
+  b.ld = m->ld;
+  b.step = m->shard_stride == 0 ? bcols : m->shard_stride;
+  b.dtype = m->dtype;
+  b.base = static_cast<const char*>(m->ptr) + first * b.step * elt_size(m->dtype);
+  return b;
+}
+
+Blocks row_blocks(const tp_matrix* m, int64_t first, int64_t brows) {
+  Blocks b;
+  b.ld = m->ld;
+  b.step = m->shard_stride == 0 ? brows * m->ld : m->shard_stride;
+  b.dtype = m->dtype;
+  b.base = static_cast<const char*>(m->ptr) + first * b.step * elt_size(m->dtype);
+  return b;
+}
+
+Range blocks_range(const Blocks& b, int64_t ns, int64_t brows, int64_t bcols) {
+  return range_of(b.base, b.dtype, ns, b.step, brows, bcols, b.ld);
+}
+
+// A batched product over ns shards: C_j = op(A_j) op(B_j), block j of each
+// operand `step` elements after block j-1.
+GemmDesc product(const Blocks& a, bool a_trans, const Blocks& b, bool b_trans, const Blocks& c, int64_t M,
+                 int64_t N, int64_t K, int64_t batch, bool in_bf16) {
+  GemmDesc g;
+  std::memset(&g, 0, sizeof(g));
+  g.A = a.base;
+  g.lda = a.ld;
+  g.sA = a.step;
+  g.a_trans = a_trans;
+  g.B = b.base;
+  g.ldb = b.ld;
+  g.sB = b.step;
+  g.b_trans = b_trans;
+  g.C = const_cast<char*>(c.base);
+  g.ldc = c.ld;
+  g.sC = c.step;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.batch = (int32_t)batch;
+  g.in_bf16 = in_bf16;
+  g.out_kind = c.dtype == TP_BF16 ? tp::OUT_BF16 : tp::OUT_F32;
+  g.act = tp::ACT_NONE;
+  return g;
+}
+
+Blocks whole(const tp_matrix* m) {
+  Blocks b;
+  b.base = static_cast<const char*>(m->ptr);
+  b.ld = m->ld;
+  b.step = 0;
+  b.dtype = m->dtype;
+  return b;
+}
+
+Blocks buffer_blocks(void* ptr, int32_t dtype, int64_t ld, int64_t step) {
+  Blocks b;
+  b.base = static_cast<const char*>(ptr);
+  b.ld = ld;
+  b.step = step;
+  b.dtype = dtype;
+  return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,6 +442,271 @@ tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, i
     cd.ldy = Y->ld;
     cd.n = ns;
     if ((e = tp::launch_combine(cd, s)) != hipSuccess) return TP_ERR_HIP;
+  }
+  return TP_OK;
+}
+
+tp_status tp_col_linear_backward(const tp_matrix* X, const tp_matrix* W, const tp_matrix* dY, int32_t N,
+                                 int32_t s0, int32_t ns, const tp_matrix* dXp, const tp_matrix* dW,
+                                 void* stream) {
+  if (!X || !W || !dY || (!dXp && !dW)) return TP_ERR_NULL;
+  if (!valid_dtype(X->dtype) || !valid_dtype(W->dtype) || !valid_dtype(dY->dtype)) return TP_ERR_DTYPE;
+  if (X->dtype != W->dtype || X->dtype != dY->dtype) return TP_ERR_DTYPE;
+  if (dXp && dXp->dtype != TP_F32) return TP_ERR_DTYPE;
+  if (dW && !valid_dtype(dW->dtype)) return TP_ERR_DTYPE;
+  if (X->rows < 0 || X->cols < 0 || W->rows < 0 || W->cols < 0 || dY->rows < 0 || dY->cols < 0) return TP_ERR_SHAPE;
+  if (N < 1 || W->cols % N != 0) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int64_t M = X->rows, K = X->cols, width = W->cols / N;
+  if (W->rows != K || dY->rows != M || dY->cols != (int64_t)ns * width) return TP_ERR_SHAPE;
+  if (dXp && (dXp->rows != M || dXp->cols != K)) return TP_ERR_SHAPE;
+  if (dW && (dW->rows != K || dW->cols != (int64_t)ns * width)) return TP_ERR_SHAPE;
+  if (X->shard_stride != 0) return TP_ERR_STRIDE;
+  if (dXp && ns > 1 && dXp->shard_stride == 0 && M > 0 && K > 0) return TP_ERR_STRIDE;
+  tp_status st;
+  if ((st = check_matrix(X, 1, M, K, K)) != TP_OK) return st;
+  if ((st = check_matrix(W, ns, K, width, W->cols)) != TP_OK) return st;
+  if ((st = check_matrix(dY, ns, M, width, dY->cols)) != TP_OK) return st;
+  if (dXp && (st = check_matrix(dXp, ns, M, K, K)) != TP_OK) return st;
+  if (dW && (st = check_matrix(dW, ns, K, width, dW->cols)) != TP_OK) return st;
+
+  const bool bf16 = X->dtype == TP_BF16;
+  const Blocks wb = col_blocks(W, s0, width), yb = col_blocks(dY, 0, width);
+  const Range xr = range_of(X->ptr, X->dtype, 1, 0, M, K, X->ld);
+  const Range wr = blocks_range(wb, ns, K, width), yr = blocks_range(yb, ns, M, width);
+  Range pr, gr;
+  if (dXp) {
+    pr = range_of(dXp->ptr, dXp->dtype, ns, dXp->shard_stride, M, K, dXp->ld);
+    if (overlaps(pr, xr) || overlaps(pr, wr) || overlaps(pr, yr)) return TP_ERR_ALIAS;
+  }
+  if (dW) {
+    gr = blocks_range(col_blocks(dW, 0, width), ns, K, width);
+    if (overlaps(gr, xr) || overlaps(gr, wr) || overlaps(gr, yr) || overlaps(gr, pr)) return TP_ERR_ALIAS;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dXp) {
+    // P_j = dY_j W_s^T: W_s stored [K, width] is the transposed right operand
+    const Blocks pb = buffer_blocks(dXp->ptr, TP_F32, dXp->ld, dXp->shard_stride);
+    const GemmDesc g = product(yb, false, wb, true, pb, M, K, width, ns, bf16);
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+  }
+  if (dW) {
+    // dW_j = X^T dY_j: X stored [M, K] is the transposed left operand
+    const Blocks gb = col_blocks(dW, 0, width);
+    GemmDesc g = product(whole(X), true, yb, false, gb, K, width, M, ns, bf16);
+    if (dY->shard_stride == 0 && dW->shard_stride == 0) {
+      g.N = (int64_t)ns * width;  // side-by-side shards form one product
+      g.batch = 1;
+    }
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+  }
+  return TP_OK;
+}
+
+tp_status tp_row_linear_backward(const tp_matrix* X, const tp_matrix* W, const tp_matrix* dY, int32_t N,
+                                 int32_t s0, int32_t ns, const tp_matrix* dX, const tp_matrix* dW,
+                                 void* stream) {
+  if (!X || !W || !dY || (!dX && !dW)) return TP_ERR_NULL;
+  if (!valid_dtype(X->dtype) || !valid_dtype(W->dtype) || !valid_dtype(dY->dtype)) return TP_ERR_DTYPE;
+  if (X->dtype != W->dtype || X->dtype != dY->dtype) return TP_ERR_DTYPE;
+  if ((dX && !valid_dtype(dX->dtype)) || (dW && !valid_dtype(dW->dtype))) return TP_ERR_DTYPE;
+  if (X->rows < 0 || X->cols < 0 || W->rows < 0 || W->cols < 0 || dY->rows < 0 || dY->cols < 0) return TP_ERR_SHAPE;
+  if (N < 1 || X->cols % N != 0) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int64_t M = X->rows, K = X->cols, kb = K / N, Nout = W->cols;
+  if (W->rows != K || dY->rows != M || dY->cols != Nout) return TP_ERR_SHAPE;
+  if (dX && (dX->rows != M || dX->cols != (int64_t)ns * kb)) return TP_ERR_SHAPE;
+  if (dW && (dW->rows != (int64_t)ns * kb || dW->cols != Nout)) return TP_ERR_SHAPE;
+  if (dY->shard_stride != 0) return TP_ERR_STRIDE;
+  tp_status st;
+  if ((st = check_matrix(X, ns, M, kb, K)) != TP_OK) return st;
+  if ((st = check_matrix(W, ns, kb, Nout, Nout)) != TP_OK) return st;
+  if ((st = check_matrix(dY, 1, M, Nout, Nout)) != TP_OK) return st;
+  if (dX && (st = check_matrix(dX, ns, M, kb, dX->cols)) != TP_OK) return st;
+  if (dW && (st = check_matrix(dW, ns, kb, Nout, Nout)) != TP_OK) return st;
+
+  const bool bf16 = X->dtype == TP_BF16;
+  const Blocks xb = col_blocks(X, s0, kb), wb = row_blocks(W, s0, kb);
+  const Range xr = blocks_range(xb, ns, M, kb), wr = blocks_range(wb, ns, kb, Nout);
+  const Range yr = range_of(dY->ptr, dY->dtype, 1, 0, M, Nout, dY->ld);
+  Range ar, gr;
+  if (dX) {
+    ar = blocks_range(col_blocks(dX, 0, kb), ns, M, kb);
+    if (overlaps(ar, xr) || overlaps(ar, wr) || overlaps(ar, yr)) return TP_ERR_ALIAS;
+  }
+  if (dW) {
+    gr = blocks_range(row_blocks(dW, 0, kb), ns, kb, Nout);
+    if (overlaps(gr, xr) || overlaps(gr, wr) || overlaps(gr, yr) || overlaps(gr, ar)) return TP_ERR_ALIAS;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dX) {
+    // dX_j = dY W_s^T: W_s stored [kb, Nout] is the transposed right operand
+    GemmDesc g = product(whole(dY), false, wb, true, col_blocks(dX, 0, kb), M, kb, Nout, ns, bf16);
+    if (W->shard_stride == 0 && dX->shard_stride == 0) {
+      g.N = (int64_t)ns * kb;  // consecutive row blocks of W give side-by-side blocks of dX
+      g.batch = 1;
+    }
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+  }
+  if (dW) {
+    // dW_j = X_s^T dY: X_s stored [M, kb] is the transposed left operand
+    GemmDesc g = product(xb, true, whole(dY), false, row_blocks(dW, 0, kb), kb, Nout, M, ns, bf16);
+    if (X->shard_stride == 0 && dW->shard_stride == 0) {
+      g.M = (int64_t)ns * kb;  // side-by-side column blocks of X give stacked row blocks of dW
+      g.batch = 1;
+    }
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+  }
+  return TP_OK;
+}
+
+tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, const tp_matrix* dY,
+                          int32_t N, int32_t s0, int32_t ns, int32_t act, void* workspace,
+                          size_t* workspace_bytes, const tp_matrix* dX, const tp_matrix* dW1,
+                          const tp_matrix* dW2, void* stream) {
+  if (!X || !W1 || !W2 || !dY || !workspace_bytes || (!dX && !dW1 && !dW2)) return TP_ERR_NULL;
+  if (!valid_dtype(X->dtype) || !valid_dtype(W1->dtype) || !valid_dtype(W2->dtype) || !valid_dtype(dY->dtype))
+    return TP_ERR_DTYPE;
+  if (X->dtype != W1->dtype || X->dtype != W2->dtype || X->dtype != dY->dtype) return TP_ERR_DTYPE;
+  if (dX && dX->dtype != TP_F32) return TP_ERR_DTYPE;
+  if ((dW1 && !valid_dtype(dW1->dtype)) || (dW2 && !valid_dtype(dW2->dtype))) return TP_ERR_DTYPE;
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU) return TP_ERR_SHAPE;
+  if (X->rows < 0 || X->cols < 0 || W1->rows < 0 || W1->cols < 0 || W2->rows < 0 || W2->cols < 0 ||
+      dY->rows < 0 || dY->cols < 0)
+    return TP_ERR_SHAPE;
+  if (N < 1 || W1->cols % N != 0) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int64_t M = X->rows, d = X->cols, F = W1->cols, width = F / N, Dout = W2->cols;
+  const int64_t hcols = (int64_t)ns * width;
+  if (W1->rows != d || W2->rows != F || dY->rows != M || dY->cols != Dout) return TP_ERR_SHAPE;
+  if (dX && (dX->rows != M || dX->cols != d)) return TP_ERR_SHAPE;
+  if (dW1 && (dW1->rows != d || dW1->cols != hcols)) return TP_ERR_SHAPE;
+  if (dW2 && (dW2->rows != hcols || dW2->cols != Dout)) return TP_ERR_SHAPE;
+  if (X->shard_stride != 0 || dY->shard_stride != 0 || (dX && dX->shard_stride != 0)) return TP_ERR_STRIDE;
+  const bool query = workspace == nullptr;
+  tp_status st;
+  if ((st = check_matrix(X, 1, M, d, d, !query)) != TP_OK) return st;
+  if ((st = check_matrix(W1, ns, d, width, F, !query)) != TP_OK) return st;
+  if ((st = check_matrix(W2, ns, width, Dout, Dout, !query)) != TP_OK) return st;
+  if ((st = check_matrix(dY, 1, M, Dout, Dout, !query)) != TP_OK) return st;
+  if (dX && (st = check_matrix(dX, 1, M, d, d, !query)) != TP_OK) return st;
+  if (dW1 && (st = check_matrix(dW1, ns, d, width, hcols, !query)) != TP_OK) return st;
+  if (dW2 && (st = check_matrix(dW2, ns, width, Dout, Dout, !query)) != TP_OK) return st;
+
+  // Workspace, each part 256-byte aligned: Z (GeLU only), H, dZ (when dX or
+  // dW1 is wanted), all [M, ns * width] in the input dtype with shard j at
+  // column j * width; then the fp32 partials of dX [ns][M][d] when ns > 1.
+  const bool bf16 = X->dtype == TP_BF16;
+  const int32_t hdt = bf16 ? TP_BF16 : TP_F32;
+  const bool gelu = act == TP_ACT_GELU;
+  const bool need_dz = dX || dW1;
+  const size_t bytes_hc = align_up((size_t)(M * hcols * elt_size(hdt)), 256);
+  const size_t off_z = 0;
+  const size_t off_h = off_z + (gelu ? bytes_hc : 0);
+  const size_t off_dz = off_h + bytes_hc;
+  const size_t off_p = off_dz + (need_dz ? bytes_hc : 0);
+  const size_t bytes_p = dX && ns > 1 ? align_up((size_t)ns * M * d * sizeof(float), 256) : 0;
+  const size_t need = off_p + bytes_p;
+  if (query) {
+    *workspace_bytes = need > 0 ? need : 256;
+    return TP_OK;
+  }
+  if (*workspace_bytes < need) return TP_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  const Blocks w1b = col_blocks(W1, s0, width), w2b = row_blocks(W2, s0, width);
+  const Range xr = range_of(X->ptr, X->dtype, 1, 0, M, d, X->ld);
+  const Range yr = range_of(dY->ptr, dY->dtype, 1, 0, M, Dout, dY->ld);
+  const Range w1r = blocks_range(w1b, ns, d, width), w2r = blocks_range(w2b, ns, width, Dout);
+  const Range wsr{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + need};
+  Range outs[3];
+  int nout = 0;
+  if (dX) outs[nout++] = range_of(dX->ptr, dX->dtype, 1, 0, M, d, dX->ld);
+  if (dW1) outs[nout++] = blocks_range(col_blocks(dW1, 0, width), ns, d, width);
+  if (dW2) outs[nout++] = blocks_range(row_blocks(dW2, 0, width), ns, width, Dout);
+  if (overlaps(wsr, xr) || overlaps(wsr, yr) || overlaps(wsr, w1r) || overlaps(wsr, w2r)) return TP_ERR_ALIAS;
+  for (int i = 0; i < nout; ++i) {
+    if (overlaps(outs[i], xr) || overlaps(outs[i], yr) || overlaps(outs[i], w1r) || overlaps(outs[i], w2r) ||
+        overlaps(outs[i], wsr))
+      return TP_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return TP_ERR_ALIAS;
+  }
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // Shard j of Z, H and dZ: columns j * width of an [M, hcols] buffer.
+  const Blocks zb = buffer_blocks(ws + off_z, hdt, hcols, width);
+  const Blocks hb = buffer_blocks(ws + off_h, hdt, hcols, width);
+  const Blocks dzb = buffer_blocks(ws + off_dz, hdt, hcols, width);
+  const bool w1_contig = W1->shard_stride == 0, w2_contig = W2->shard_stride == 0;
+
+  // 1. Recompute H_j = act(X W1_j), keeping Z_j for the GeLU derivative.
+  {
+    GemmDesc g = product(whole(X), false, w1b, false, hb, M, width, d, ns, bf16);
+    g.sA = 0;
+    if (w1_contig) {
+      g.N = hcols;
+      g.batch = 1;
+    }
+    if (gelu) {
+      g.act = tp::ACT_GELU_SAVE;
+      g.aux = ws + off_z;
+      g.ldx = hcols;
+      g.sX = g.batch > 1 ? width : 0;
+    }
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+  }
+  // 2. dZ_j = (dY W2_j^T) * act'(Z_j).
+  if (need_dz) {
+    GemmDesc g = product(whole(dY), false, w2b, true, dzb, M, width, Dout, ns, bf16);
+    if (w2_contig) {
+      g.N = hcols;
+      g.batch = 1;
+    }
+    if (gelu) {
+      g.act = tp::ACT_DGELU;
+      g.aux = ws + off_z;
+      g.ldx = hcols;
+      g.sX = g.batch > 1 ? width : 0;
+    }
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+  }
+  // 3. dW2_j = H_j^T dY.
+  if (dW2) {
+    GemmDesc g = product(hb, true, whole(dY), false, row_blocks(dW2, 0, width), width, Dout, M, ns, bf16);
+    if (dW2->shard_stride == 0) {
+      g.M = hcols;
+      g.batch = 1;
+    }
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+  }
+  // 4. dX = sum_j dZ_j W1_j^T: fp32 partials, then the fixed-order sum.
+  if (dX) {
+    const Blocks pb = ns > 1 ? buffer_blocks(ws + off_p, TP_F32, d, M * d) : buffer_blocks(dX->ptr, TP_F32, dX->ld, 0);
+    const GemmDesc g = product(dzb, false, w1b, true, pb, M, d, width, ns, bf16);
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
+    if (ns > 1) {
+      CombineDesc cd;
+      std::memset(&cd, 0, sizeof(cd));
+      cd.P = ws + off_p;
+      cd.Y = dX->ptr;
+      cd.rows = M;
+      cd.cols = d;
+      cd.ldp = d;
+      cd.sP = M * d;
+      cd.ldy = dX->ld;
+      cd.n = ns;
+      if (tp::launch_combine(cd, s) != hipSuccess) return TP_ERR_HIP;
+    }
+  }
+  // 5. dW1_j = X^T dZ_j.
+  if (dW1) {
+    GemmDesc g = product(whole(X), true, dzb, false, col_blocks(dW1, 0, width), d, width, M, ns, bf16);
+    if (dW1->shard_stride == 0) {
+      g.N = hcols;
+      g.batch = 1;
+    }
+    if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
   }
   return TP_OK;
 }

@@ -8,12 +8,22 @@
 namespace tp {
 
 enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1 };
-enum ActKind : int { ACT_NONE = 0, ACT_GELU = 1 };
+// Epilogue applied to the fp32 accumulator v of output (m, n):
+//   ACT_NONE       C = v
+//   ACT_GELU       C = GeLU(v)
+//   ACT_GELU_SAVE  C = GeLU(v) and aux = v (bf16): the forward of the MLP's
+//                  first product, keeping the pre-activation for the backward
+//   ACT_DGELU      C = v * GeLU'(aux[m][n]) with aux bf16: the backward of GeLU
+enum ActKind : int { ACT_NONE = 0, ACT_GELU = 1, ACT_GELU_SAVE = 2, ACT_DGELU = 3 };
 
-// A batch of `batch` independent products C_z = act(A_z * B_z), z = 0..batch-1,
-// each A_z [M, K] (row stride lda), B_z [K, N] (row stride ldb), C_z [M, N]
-// (row stride ldc), with A_z = A + z * sA elements and likewise for B and C.
-// For the sharded layers z is the shard index within the executed range.
+// A batch of `batch` independent products C_z = act(op(A_z) * op(B_z)),
+// z = 0..batch-1, with op(A_z) [M, K], op(B_z) [K, N] and C_z [M, N] (row
+// stride ldc); A_z = A + z * sA elements and likewise for B, C and aux.
+// Storage is row-major: A_z is [M, K] with row stride lda, or [K, M] when
+// a_trans; B_z is [K, N] with row stride ldb, or [N, K] when b_trans. The
+// backward products use the transposed forms: dX = dY W^T (b_trans) and
+// dW = X^T dY (a_trans). For the sharded layers z is the shard index within
+// the executed range.
 struct GemmDesc {
   const void* A;
   const void* B;
@@ -25,6 +35,11 @@ struct GemmDesc {
   int32_t in_bf16;   // 1: A and B are bf16, 0: fp32
   int32_t out_kind;  // OutKind
   int32_t act;       // ActKind
+  int32_t a_trans;   // 1: A stored [K, M]
+  int32_t b_trans;   // 1: B stored [N, K]
+  void* aux;         // [M, N] per z in the input dtype (row stride ldx, z stride sX):
+                     // ACT_GELU_SAVE output, ACT_DGELU input
+  int64_t ldx, sX;
 };
 
 // Sum or concatenation of n fp32 / bf16 blocks [rows, cols] (see tp_reduce_partials).
@@ -66,9 +81,26 @@ __device__ __forceinline__ float gelu(float x) {
   return x * (x >= 0.0f ? 1.0f - hq : hq);
 }
 
+// Derivative of the GeLU above: GeLU'(x) = Phi(x) + x phi(x), phi the standard
+// normal density exp(-x^2 / 2) / sqrt(2 pi); Phi and exp(-x^2 / 2) come from
+// the same Abramowitz & Stegun evaluation.
+__device__ __forceinline__ float gelu_grad(float x) {
+  const float u = __builtin_fabsf(x) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, u, 1.0f));
+  float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  p = __builtin_fmaf(p, t, 1.421413741f);
+  p = __builtin_fmaf(p, t, -0.284496736f);
+  p = __builtin_fmaf(p, t, 0.254829592f);
+  p *= t;
+  const float e = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170368f);
+  const float hq = 0.5f * p * e;
+  const float cdf = x >= 0.0f ? 1.0f - hq : hq;
+  return __builtin_fmaf(x * 0.39894228040143267794f, e, cdf);
+}
+
 // Large-tile bf16 matrix-core GEMM. Requirements checked by the caller
-// (gemm_mfma_supported): bf16 inputs, K, N, lda, ldb, sA, sB multiples of 8,
-// 16-byte aligned A and B.
+// (gemm_mfma_supported): bf16 inputs, K, N, lda, ldb, sA, sB multiples of 8
+// (and M when a_trans), 16-byte aligned A and B.
 bool gemm_mfma_supported(const GemmDesc& d);
 hipError_t launch_gemm_mfma(const GemmDesc& d, hipStream_t stream);
 
