@@ -165,3 +165,94 @@ def test_mlp_decode_workspace_covers_intermediate_and_partials(lib):
     st, size = mlp_query(lib, X, W1, W2, N, 0, N, Y)
     assert st == 0
     assert size >= M * F * 2 + N * M * d * 4
+
+
+# ----------------------------------------------------------------------------- backward entry points
+
+
+def colb(lib, X, W, dY, N, s0, ns, dXp, dW):
+    r = lambda m: ctypes.byref(m) if m is not None else None  # noqa: E731
+    return lib.tp_col_linear_backward(r(X), r(W), r(dY), N, s0, ns, r(dXp), r(dW), None)
+
+
+def rowb(lib, X, W, dY, N, s0, ns, dX, dW):
+    r = lambda m: ctypes.byref(m) if m is not None else None  # noqa: E731
+    return lib.tp_row_linear_backward(r(X), r(W), r(dY), N, s0, ns, r(dX), r(dW), None)
+
+
+def test_col_linear_backward_validation(lib):
+    # X [4, 8], W [8, 16] split in 2 -> dY [4, 16], partials 2 x [4, 8], dW [8, 16]
+    X = m(rows=4, cols=8)
+    W = m(FAKE + (1 << 20), rows=8, cols=16)
+    dY = m(FAKE + (2 << 20), rows=4, cols=16)
+    P = m(FAKE + (3 << 20), dtype=F32, rows=4, cols=8, stride=32)
+    G = m(FAKE + (4 << 20), dtype=F32, rows=8, cols=16)
+    assert colb(lib, X, W, dY, 2, 0, 2, None, None) == 1  # no output requested
+    assert colb(lib, None, W, dY, 2, 0, 2, P, G) == 1
+    assert colb(lib, X, W, m(FAKE + (2 << 20), dtype=F32, rows=4, cols=16), 2, 0, 2, P, G) == 2  # dY dtype
+    assert colb(lib, X, W, dY, 2, 0, 2, m(FAKE + (3 << 20), rows=4, cols=8, stride=32), G) == 2  # bf16 partials
+    assert colb(lib, X, W, m(FAKE + (2 << 20), rows=4, cols=8), 2, 0, 2, P, G) == 3  # dY.cols != ns*width
+    assert colb(lib, X, W, dY, 2, 0, 2, P, m(FAKE + (4 << 20), dtype=F32, rows=8, cols=8)) == 3  # dW shape
+    assert colb(lib, X, W, dY, 3, 0, 3, P, G) == 4
+    assert colb(lib, X, W, dY, 2, 1, 2, P, G) == 5
+    assert colb(lib, X, W, dY, 2, 0, 2, m(FAKE + (3 << 20), dtype=F32, rows=4, cols=8, stride=0), G) == 6
+    assert colb(lib, X, W, dY, 2, 0, 2, P, m(FAKE + 8, dtype=F32, rows=8, cols=16)) == 7  # dW over X
+    assert colb(lib, X, W, dY, 2, 0, 2, m(FAKE + (2 << 20), dtype=F32, rows=4, cols=8, stride=32), G) == 7  # P over dY
+    assert colb(lib, X, W, dY, 2, 0, 2, P, m(FAKE + (3 << 20), dtype=F32, rows=8, cols=16)) == 7  # dW over P
+
+
+def test_row_linear_backward_validation(lib):
+    # X [4, 8] split in 2 along K, W [8, 16] -> dY [4, 16], dX [4, 8], dW [8, 16]
+    X = m(rows=4, cols=8)
+    W = m(FAKE + (1 << 20), rows=8, cols=16)
+    dY = m(FAKE + (2 << 20), rows=4, cols=16)
+    A = m(FAKE + (3 << 20), dtype=F32, rows=4, cols=8)
+    G = m(FAKE + (4 << 20), dtype=F32, rows=8, cols=16)
+    assert rowb(lib, X, W, dY, 2, 0, 2, None, None) == 1
+    assert rowb(lib, X, W, m(FAKE + (2 << 20), dtype=F32, rows=4, cols=16), 2, 0, 2, A, G) == 2
+    assert rowb(lib, X, W, m(FAKE + (2 << 20), rows=4, cols=8), 2, 0, 2, A, G) == 3  # dY.cols != Nout
+    assert rowb(lib, X, W, dY, 2, 0, 1, A, G) == 3  # one shard: dX must be [4, 4]
+    assert rowb(lib, X, W, dY, 3, 0, 3, A, G) == 4
+    assert rowb(lib, X, W, dY, 2, 0, 3, A, G) == 5
+    assert rowb(lib, X, W, m(FAKE + (2 << 20), rows=4, cols=16, stride=64), 2, 0, 2, A, G) == 6  # dY shard-major
+    assert rowb(lib, X, W, dY, 2, 0, 2, m(FAKE + 16, dtype=F32, rows=4, cols=8), G) == 7  # dX over X
+    assert rowb(lib, X, W, dY, 2, 0, 2, A, m(FAKE + (3 << 20), dtype=F32, rows=8, cols=16)) == 7  # dW over dX
+
+
+def mlpb_query(lib, X, W1, W2, dY, N, s0, ns, act, dX, dW1, dW2):
+    size = ctypes.c_size_t(0)
+    r = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    st = lib.tp_mlp_backward(r(X), r(W1), r(W2), r(dY), N, s0, ns, act, None, ctypes.byref(size), r(dX), r(dW1),
+                             r(dW2), None)
+    return st, size.value
+
+
+def test_mlp_backward_validation_and_workspace(lib):
+    M, d, F, N = 64, 32, 128, 4
+    X = m(FAKE, rows=M, cols=d)
+    W1 = m(FAKE + (1 << 20), rows=d, cols=F)
+    W2 = m(FAKE + (2 << 20), rows=F, cols=d)
+    dY = m(FAKE + (3 << 20), rows=M, cols=d)
+    dX = m(FAKE + (4 << 20), dtype=F32, rows=M, cols=d)
+    dW1 = m(FAKE + (5 << 20), dtype=F32, rows=d, cols=F)
+    dW2 = m(FAKE + (6 << 20), dtype=F32, rows=F, cols=d)
+    hc = M * F * 2  # one [M, ns*width] bf16 buffer (Z, H or dZ)
+    st, size = mlpb_query(lib, X, W1, W2, dY, N, 0, N, 1, dX, dW1, dW2)
+    assert st == 0 and size == 3 * hc + N * M * d * 4  # Z, H, dZ and the dX partials
+    st, size = mlpb_query(lib, X, W1, W2, dY, N, 0, N, 0, dX, dW1, dW2)
+    assert st == 0 and size == 2 * hc + N * M * d * 4  # no activation: no Z
+    st, size = mlpb_query(lib, X, W1, W2, dY, N, 0, N, 1, None, None, dW2)
+    assert st == 0 and size == 2 * hc  # dW2 alone needs Z and H only
+    st, size = mlpb_query(lib, X, W1, W2, dY, N, 3, 1, 1, dX, m(FAKE + (5 << 20), dtype=F32, rows=d, cols=F // N),
+                          m(FAKE + (6 << 20), dtype=F32, rows=F // N, cols=d))
+    assert st == 0 and size == 3 * (M * (F // N) * 2)  # one shard writes dX directly
+    assert mlpb_query(lib, X, W1, W2, dY, N, 0, N, 1, None, None, None)[0] == 1
+    assert mlpb_query(lib, X, W1, W2, dY, 3, 0, 3, 1, dX, dW1, dW2)[0] == 4
+    assert mlpb_query(lib, X, W1, W2, dY, N, 0, N, 5, dX, dW1, dW2)[0] == 3
+    assert mlpb_query(lib, X, W1, W2, dY, N, 0, N, 1, m(FAKE + (4 << 20), rows=M, cols=d), dW1, dW2)[0] == 2
+    assert mlpb_query(lib, X, W1, W2, m(FAKE + (3 << 20), rows=M, cols=d + 8), N, 0, N, 1, dX, dW1, dW2)[0] == 3
+    size = ctypes.c_size_t(16)
+    r = ctypes.byref
+    st = lib.tp_mlp_backward(r(X), r(W1), r(W2), r(dY), N, 0, N, 1, ctypes.c_void_p(FAKE + (9 << 20)), r(size),
+                             r(dX), r(dW1), r(dW2), None)
+    assert st == 8  # workspace too small
