@@ -33,6 +33,8 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (256 CU x 4096 f
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth
 LEAD_CYCLES = 40_000_000  # ~20 ms of GPU spin at the ~2 GHz shader clock
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# Workloads that reuse the shapes of another one.
+BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp"}
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
 # peak under "roofline"), with the decode-shaped MLP's HBM GB/s beside it.
 METRIC = "sharded-linear TFLOP/s (% of bf16 MFMA peak); decode-shape HBM GB/s"
@@ -66,7 +68,7 @@ def make_inputs(name, torch, dev):
     """Seeded synthetic inputs of one workload, uploaded as bf16 bit patterns."""
     from synthetic import WORKLOADS, normal_bf16
 
-    wl = WORKLOADS[name]
+    wl = WORKLOADS[BASE_WORKLOAD.get(name, name)]
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -86,6 +88,13 @@ def make_inputs(name, torch, dev):
         t["wqkv"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
         t["wo"] = up(normal_bf16((wl.d, wl.out), 0.02, wl.wid, 2)[0])
         t["a"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 3)[0])
+    elif name == "megatron_mlp_bwd":
+        wl = WORKLOADS["megatron_mlp"]
+        t["wl"] = wl
+        t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
+        t["w1"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
+        t["w2"] = up(normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)[0])
+        t["dy"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 4)[0])
     elif name == "decode_mlp":
         width = wl.F // wl.N
         t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
@@ -150,6 +159,21 @@ def plan(name, t, torch, tp):
             tp.row_linear(t["a"], t["wo"], wl.N, out=p)
             rec()
             tp.reduce_partials(p, "rows", out=y)
+            rec()
+
+        return kernels, step
+    if name == "megatron_mlp_bwd":
+        dx = torch.empty((wl.M, wl.d), dtype=torch.float32, device=dev)
+        dw1 = torch.empty((wl.d, wl.F), dtype=torch.float32, device=dev)
+        dw2 = torch.empty((wl.F, wl.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(tp.mlp_backward_workspace_bytes(t["x"], t["w1"], t["w2"], t["dy"], wl.N), dtype=torch.uint8,
+                         device=dev)
+        # recompute Z and H, dZ = (dY W2^T) * GeLU'(Z), dW2 = H^T dY, dX partials + sum, dW1 = X^T dZ
+        kernels = [{"name": "mlp_backward", "flop": 5 * flop(wl.M, wl.d, wl.F), "bound": "mfma",
+                    "bytes": 2.0 * (wl.M * wl.d * 2 + 2 * wl.d * wl.F) + 4.0 * (wl.M * wl.d + 2 * wl.d * wl.F)}]
+
+        def step(i, rec):
+            tp.mlp_backward(t["x"], t["w1"], t["w2"], t["dy"], wl.N, dx=dx, dw1=dw1, dw2=dw2, workspace=ws)
             rec()
 
         return kernels, step
@@ -298,7 +322,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp"])
+                    choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp",
+                             "megatron_mlp_bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for HBM counter calibration)")
@@ -319,7 +344,7 @@ def main():
     tp.library()  # fails loudly if the HIP library is missing
     main_name = "megatron_mlp" if args.workload in ("all", "megatron_mlp") else args.workload
     names = [main_name] if args.workload != "all" else ["megatron_mlp", "attn_proj", "gpt3_mlp_shard",
-                                                        "decode_mlp"]
+                                                        "decode_mlp", "megatron_mlp_bwd"]
     results = {}
     for name in names:
         steps = args.steps if name in ("megatron_mlp", "decode_mlp") else max(3, args.steps // 5)
@@ -331,7 +356,7 @@ def main():
     main = results[main_name]
     from synthetic import WORKLOADS
 
-    wl = WORKLOADS[main_name]
+    wl = WORKLOADS[BASE_WORKLOAD.get(main_name, main_name)]
     metric = METRIC
     if main_name == "decode_mlp":
         unit, value = "GB/s", main["gbs"]
