@@ -61,6 +61,9 @@ __all__ = [
     "col_linear_backward",
     "row_linear_backward",
     "mlp_backward",
+    "attention_shard",
+    "attention",
+    "shard_qkv_columns",
 ]
 
 ACTS = ("none", "gelu")
@@ -304,3 +307,93 @@ def mlp_backward(x, w1, w2, dy, n: int, act: str = "gelu", s0: int = 0, ns: int 
         dw1.append(matmul(transpose(x), dz))
         partials.append(matmul(dz, transpose(w1s)))
     return reduce_sum(partials), concat_cols(dw1), np.vstack(dw2)
+
+
+# ----------------------------------------------------------------------------- attention per head subset
+#
+# [TP-topic] figure "Tensor Parallelism — Split Layers Across GPUs", panel
+# "Attention Head Parallelism": the heads are split evenly over the shards and
+# each shard computes full attention for its own heads (the heads do not
+# interact); with grouped-query attention the query heads are split evenly and
+# the shared key/value heads are replicated. Section "Megatron-LM Tensor
+# Parallelism": the Q, K, V projections are split by columns (so each shard's
+# block of the fused QKV output holds its own heads) and the output projection
+# by rows. Readings taken where the pages are silent: a shard's QKV block holds
+# its query heads, then its key heads, then its value heads, head-major with
+# head_dim columns each; scores are scaled by 1/sqrt(head_dim); the model is a
+# decoder (causal: a token attends to itself and earlier tokens of its own
+# sequence) unless causal is False; tokens are consecutive sequences of
+# seq_len tokens; query head h of a shard uses key/value head h // (hq / hkv).
+
+
+def _softmax_rows(s) -> np.ndarray:
+    """exp(s - max) / sum, row by row; -inf entries contribute zero."""
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=1, keepdims=True)
+
+
+def attention_shard(qkv_block, hq: int, hkv: int, head_dim: int, seq_len: int, causal: bool = True) -> np.ndarray:
+    """Attention of one shard's heads: qkv_block [M, (hq + 2 hkv) head_dim] -> [M, hq head_dim], float64."""
+    qkv_block = widen(qkv_block)
+    m_rows = qkv_block.shape[0]
+    if qkv_block.shape[1] != (hq + 2 * hkv) * head_dim:
+        raise ValueError("QKV block width does not match the head counts")
+    if hkv < 1 or hq % hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    if seq_len < 1 or m_rows % seq_len != 0:
+        raise ValueError("tokens must be whole sequences")
+    group = hq // hkv
+    out = np.zeros((m_rows, hq * head_dim))
+    koff, voff = hq * head_dim, (hq + hkv) * head_dim
+    for r0 in range(0, m_rows, seq_len):
+        rows = slice(r0, r0 + seq_len)
+        for h in range(hq):
+            kv = h // group
+            q = qkv_block[rows, h * head_dim:(h + 1) * head_dim]
+            k = qkv_block[rows, koff + kv * head_dim:koff + (kv + 1) * head_dim]
+            v = qkv_block[rows, voff + kv * head_dim:voff + (kv + 1) * head_dim]
+            s = matmul(q, transpose(k)) / np.sqrt(head_dim)
+            if causal:
+                s = np.where(np.tril(np.ones((seq_len, seq_len), dtype=bool)), s, -np.inf)
+            out[rows, h * head_dim:(h + 1) * head_dim] = matmul(_softmax_rows(s), v)
+    return out
+
+
+def _heads_per_shard(heads: int, kv_heads: int, n: int):
+    hq = _check_split(heads, n, "query heads")
+    if kv_heads >= n:
+        hkv = _check_split(kv_heads, n, "key/value heads")
+    else:
+        if kv_heads < 1 or n % kv_heads != 0:
+            raise ValueError("shards must split the key/value heads evenly or replicate them evenly")
+        hkv = 1
+    return hq, hkv
+
+
+def attention(qkv, n: int, heads: int, kv_heads: int, head_dim: int, seq_len: int, causal: bool = True,
+              s0: int = 0, ns: int | None = None) -> np.ndarray:
+    """Attention of the executed shards, concatenated: qkv [M, ns * block] (shard j's block at
+    columns j * block, block = (hq + 2 hkv) head_dim) -> [M, ns * hq * head_dim]."""
+    ns = n - s0 if ns is None else ns
+    hq, hkv = _heads_per_shard(heads, kv_heads, n)
+    blocks = split_cols(qkv, ns)
+    return concat_cols([attention_shard(b, hq, hkv, head_dim, seq_len, causal) for b in blocks])
+
+
+def shard_qkv_columns(heads: int, kv_heads: int, head_dim: int, n: int, s: int) -> np.ndarray:
+    """Column indices, into an unsharded [Q heads | K heads | V heads] projection output, of shard s's
+    QKV block: its query heads, then its key/value heads (a replicated copy when kv_heads < n)."""
+    hq, hkv = _heads_per_shard(heads, kv_heads, n)
+    group = heads // kv_heads
+    q_heads = list(range(s * hq, (s + 1) * hq))
+    kv = sorted({h // group for h in q_heads})
+    if len(kv) != hkv:
+        raise ValueError("a shard's query heads must share its key/value heads")
+    cols = []
+    for h in q_heads:
+        cols += list(range(h * head_dim, (h + 1) * head_dim))
+    for base in (heads, heads + kv_heads):
+        for g in kv:
+            cols += list(range((base + g) * head_dim, (base + g + 1) * head_dim))
+    return np.array(cols)
