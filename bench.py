@@ -38,7 +38,7 @@ BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp"}
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
 # peak under "roofline"), with the decode-shaped MLP's HBM GB/s beside it.
 METRIC = "sharded-linear TFLOP/s (% of bf16 MFMA peak); decode-shape HBM GB/s"
-KERNEL_SOURCES = ["gemm_mfma.hip", "gemm_skinny.hip", "combine.hip"]
+KERNEL_SOURCES = ["gemm_mfma.hip", "gemm_skinny.hip", "combine.hip", "attention.hip"]
 
 
 def kernel_source_hash() -> str:

@@ -239,6 +239,32 @@ tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matr
                           size_t* workspace_bytes, const tp_matrix* dX, const tp_matrix* dW1,
                           const tp_matrix* dW2, void* stream);
 
+/*
+ * Attention for the heads of the executed shards, the step between the
+ * column-parallel QKV projection and the row-parallel output projection
+ * ([TP-topic] figure "Tensor Parallelism — Split Layers Across GPUs", panel
+ * "Attention Head Parallelism": each shard computes full attention for its
+ * own subset of heads, which do not interact; under grouped-query attention
+ * the query heads are split evenly and the shared key/value heads
+ * replicated; "Megatron-LM Tensor Parallelism", attention layer splitting).
+ * Shard s holds hq = heads/N query heads and hkv = kv_heads/N key/value heads
+ * (hkv = 1, a replicated head, when kv_heads < N). For every query head h of
+ * every executed shard and every sequence of seq_len consecutive tokens:
+ *     O_h = softmax(Q_h K_g^T / sqrt(head_dim)) V_g,   g = h / (hq / hkv),
+ * causal (token i attends to tokens 0..i of its sequence) when causal = 1.
+ *   QKV  logical [M, ns*(hq + 2 hkv)*head_dim], the layout of tp_col_linear's
+ *        Y: shard j's block holds its query heads, then its key heads, then
+ *        its value heads, head-major, head_dim columns each.
+ *   A    logical [M, ns*hq*head_dim], dtype of QKV; shard j's block holds its
+ *        query heads' outputs in order: the X of the row-parallel W_o.
+ *   M must be a multiple of seq_len. bf16 with head_dim 64 or 128 runs on the
+ *   matrix cores (fp32 scores and softmax, probabilities rounded to bf16);
+ *   other cases take an fp32 element-wise kernel limited to seq_len <= 8192
+ *   (TP_ERR_TOO_LARGE beyond).
+ */
+tp_status tp_attention(const tp_matrix* QKV, int32_t N, int32_t s0, int32_t ns, int32_t heads, int32_t kv_heads,
+                       int32_t head_dim, int64_t seq_len, int32_t causal, const tp_matrix* A, void* stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* tp_status_string(int32_t status);
 

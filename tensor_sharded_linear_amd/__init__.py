@@ -30,6 +30,7 @@ __all__ = [
     "row_linear_backward",
     "mlp_backward",
     "mlp_backward_workspace_bytes",
+    "attention",
     "TpError",
     "library",
     "version",
@@ -348,3 +349,33 @@ def mlp_backward(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, dy: torch.
                                    _ref(am), _ref(g1m), _ref(g2m), ctypes.c_void_p(_stream(x)))
     _lib.check(st, "tp_mlp_backward")
     return a, g1, g2
+
+
+# ----------------------------------------------------------------------------- attention per head subset
+
+
+def attention(qkv: torch.Tensor, n: int, heads: int, kv_heads: int, head_dim: int, seq_len: int,
+              causal: bool = True, s0: int = 0, ns: int | None = None, out: torch.Tensor | None = None,
+              partitioned: bool = False) -> torch.Tensor:
+    """Attention of the executed shards' heads (tp_attention).
+
+    qkv: [M, ns*(hq + 2 hkv)*head_dim] (column-parallel QKV output) or partitioned
+    [ns, M, (hq + 2 hkv)*head_dim]. Returns [M, ns*hq*head_dim] (or [ns, M, hq*head_dim]).
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(qkv)
+    hq = heads // n if n > 0 else 0
+    hkv = (kv_heads // n if kv_heads >= n else 1) if n > 0 else 0
+    blk = (hq + 2 * hkv) * head_dim
+    m = qkv.shape[0] if qkv.dim() == 2 else qkv.shape[1]
+    oblk = hq * head_dim
+    if out is None:
+        shape = (ns, m, oblk) if partitioned else (m, ns * oblk)
+        out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device)
+    _require_gpu(out)
+    qm = _blocks(qkv, m, ns * blk)
+    am = _blocks(out, m, ns * oblk)
+    st = library().tp_attention(ctypes.byref(qm), n, s0, ns, heads, kv_heads, head_dim, seq_len, int(bool(causal)),
+                                ctypes.byref(am), ctypes.c_void_p(_stream(qkv)))
+    _lib.check(st, "tp_attention")
+    return out

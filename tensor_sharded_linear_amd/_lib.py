@@ -38,6 +38,7 @@ EXPORTS = (
     "tp_col_linear_backward",
     "tp_row_linear_backward",
     "tp_mlp_backward",
+    "tp_attention",
     "tp_status_string",
     "tp_version",
 )
@@ -97,6 +98,9 @@ def load() -> ctypes.CDLL:
     lib.tp_mlp_backward.argtypes = [_M, _M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), _M, _M, _M, ctypes.c_void_p]
     lib.tp_mlp_backward.restype = ctypes.c_int32
+    lib.tp_attention.argtypes = [_M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _M, ctypes.c_void_p]
+    lib.tp_attention.restype = ctypes.c_int32
     lib.tp_status_string.argtypes = [ctypes.c_int32]
     lib.tp_status_string.restype = ctypes.c_char_p
     lib.tp_version.argtypes = []

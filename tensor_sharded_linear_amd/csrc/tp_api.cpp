@@ -7,6 +7,7 @@
 // shard i computes X W_i) and "Row-Wise Parallelism" (W stacked by rows, X
 // split to match, partial products summed). Shard s owns the s-th contiguous
 // block of the split dimension; the split must be even.
+#include <cmath>
 #include <cstring>
 
 #include "tp.h"
@@ -709,6 +710,51 @@ tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matr
     if (run_gemm(g, s) != hipSuccess) return TP_ERR_HIP;
   }
   return TP_OK;
+}
+
+tp_status tp_attention(const tp_matrix* QKV, int32_t N, int32_t s0, int32_t ns, int32_t heads, int32_t kv_heads,
+                       int32_t head_dim, int64_t seq_len, int32_t causal, const tp_matrix* A, void* stream) {
+  if (!QKV || !A) return TP_ERR_NULL;
+  if (!valid_dtype(QKV->dtype) || !valid_dtype(A->dtype)) return TP_ERR_DTYPE;
+  if (QKV->dtype != A->dtype) return TP_ERR_DTYPE;
+  if (QKV->rows < 0 || QKV->cols < 0 || A->rows < 0 || A->cols < 0) return TP_ERR_SHAPE;
+  if (heads < 1 || kv_heads < 1 || head_dim < 1 || seq_len < 1 || (causal != 0 && causal != 1)) return TP_ERR_SHAPE;
+  if (heads % kv_heads != 0) return TP_ERR_SHAPE;
+  if (N < 1 || heads % N != 0) return TP_ERR_INDIVISIBLE;
+  // key/value heads are split evenly, or (fewer than shards) replicated evenly
+  if (kv_heads >= N ? kv_heads % N != 0 : N % kv_heads != 0) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int32_t hq = heads / N, hkv = kv_heads >= N ? kv_heads / N : 1;
+  if (hq % hkv != 0) return TP_ERR_INDIVISIBLE;
+  const int64_t M = QKV->rows;
+  const int64_t blk = (int64_t)(hq + 2 * hkv) * head_dim, oblk = (int64_t)hq * head_dim;
+  if (QKV->cols != (int64_t)ns * blk || A->rows != M || A->cols != (int64_t)ns * oblk) return TP_ERR_SHAPE;
+  if (M % seq_len != 0) return TP_ERR_SHAPE;
+  tp_status st;
+  if ((st = check_matrix(QKV, ns, M, blk, QKV->cols)) != TP_OK) return st;
+  if ((st = check_matrix(A, ns, M, oblk, A->cols)) != TP_OK) return st;
+  const Blocks qb = col_blocks(QKV, 0, blk), ab = col_blocks(A, 0, oblk);
+  if (overlaps(blocks_range(ab, ns, M, oblk), blocks_range(qb, ns, M, blk))) return TP_ERR_ALIAS;
+  tp::AttnDesc a;
+  std::memset(&a, 0, sizeof(a));
+  a.qkv = qb.base;
+  a.ld_qkv = qb.ld;
+  a.s_qkv = qb.step;
+  a.out = const_cast<char*>(ab.base);
+  a.ld_out = ab.ld;
+  a.s_out = ab.step;
+  a.tokens = M;
+  a.seq_len = seq_len;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.head_dim = head_dim;
+  a.shards = ns;
+  a.causal = causal;
+  a.in_bf16 = QKV->dtype == TP_BF16;
+  a.scale = 1.0f / std::sqrt((float)head_dim);
+  if (M == 0) return TP_OK;
+  if (!tp::attention_mfma_supported(a) && !tp::attention_generic_supported(a)) return TP_ERR_TOO_LARGE;
+  return hip_status(tp::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 
 const char* tp_status_string(int32_t status) {

@@ -120,4 +120,22 @@ hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t stream);
 
 hipError_t launch_combine(const CombineDesc& d, hipStream_t stream);
 
+// Attention over the heads of `shards` executed shards (see tp_attention):
+// shard j's QKV block [tokens, (hq + 2 hkv) head_dim] starts s_qkv elements
+// after block j-1 (row stride ld_qkv) and its output block [tokens, hq
+// head_dim] s_out elements after block j-1 (row stride ld_out).
+struct AttnDesc {
+  const void* qkv;
+  void* out;
+  int64_t ld_qkv, s_qkv;
+  int64_t ld_out, s_out;
+  int64_t tokens, seq_len;
+  int32_t hq, hkv, head_dim, shards;
+  int32_t causal, in_bf16;
+  float scale;  // applied to the scores: 1 / sqrt(head_dim)
+};
+bool attention_mfma_supported(const AttnDesc& a);
+bool attention_generic_supported(const AttnDesc& a);
+hipError_t launch_attention(const AttnDesc& a, hipStream_t stream);
+
 }  // namespace tp

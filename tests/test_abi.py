@@ -256,3 +256,24 @@ def test_mlp_backward_validation_and_workspace(lib):
     st = lib.tp_mlp_backward(r(X), r(W1), r(W2), r(dY), N, 0, N, 1, ctypes.c_void_p(FAKE + (9 << 20)), r(size),
                              r(dX), r(dW1), r(dW2), None)
     assert st == 8  # workspace too small
+
+
+def test_attention_validation(lib):
+    # 8 heads of 16 over N = 2 shards: block = (4 + 2*4) * 16 = 192, output block 64
+    def att(qkv, n, s0, ns, heads, kv, dh, L, causal, a):
+        r = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+        return lib.tp_attention(r(qkv), n, s0, ns, heads, kv, dh, L, causal, r(a), None)
+
+    Q = m(FAKE, rows=20, cols=2 * 192)
+    A = m(FAKE + (1 << 20), rows=20, cols=2 * 64)
+    assert att(None, 2, 0, 2, 8, 8, 16, 10, 1, A) == 1
+    assert att(Q, 2, 0, 2, 8, 8, 16, 10, 1, m(FAKE + (1 << 20), dtype=F32, rows=20, cols=128)) == 2
+    assert att(Q, 2, 0, 2, 8, 8, 16, 7, 1, A) == 3       # 20 tokens are not whole sequences of 7
+    assert att(Q, 2, 0, 2, 8, 8, 16, 10, 2, A) == 3      # causal must be 0 or 1
+    assert att(Q, 2, 0, 2, 8, 3, 16, 10, 1, A) == 3      # heads not a multiple of kv_heads
+    assert att(Q, 3, 0, 3, 9, 9, 16, 10, 1, A) == 3      # block widths no longer match Q / A
+    assert att(Q, 2, 0, 2, 8, 8, 32, 10, 1, A) == 3      # head_dim 32 needs wider blocks
+    assert att(Q, 16, 0, 2, 8, 8, 16, 10, 1, A) == 4     # 16 shards do not split 8 heads
+    assert att(Q, 2, 1, 2, 8, 8, 16, 10, 1, A) == 5
+    assert att(Q, 2, 0, 2, 8, 8, 16, 10, 1, m(FAKE + 64, rows=20, cols=128)) == 7  # output over QKV
+    assert att(Q, 2, 0, 2, 8, 8, 16, 10, 1, m(FAKE + (1 << 20), rows=20, cols=128, ld=100)) == 6

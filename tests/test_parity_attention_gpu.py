@@ -1,0 +1,110 @@
+"""GPU parity of attention per head subset (tp_attention) against the float64 oracle.
+
+Seeded synthetic QKV blocks, the library on the GPU and the oracle on the CPU
+on the same bits, compared within the bars of tests/parity.py (the output is
+stored in the input dtype, bf16 here, so the bf16 storage allowance applies).
+Cases: causal and not, head_dim 128 and 64 on the matrix cores, sequence
+lengths that leave ragged 128-query and 64-key blocks, several sequences,
+grouped-query attention with key/value heads split and replicated, shard
+subsets, partitioned layouts, the element-wise path (fp32 and other head
+sizes), and the attention-projection workload's full shape checked on two
+of its eight shards.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_sharded_linear_amd as tp
+from synthetic import WORKLOADS, normal_bf16
+from parity import assert_close, bf16_tensor, f32_tensor, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def qkv_case(M, heads, kv_heads, dh, n, ns, wid, sigma=1.0):
+    hq = heads // n
+    hkv = kv_heads // n if kv_heads >= n else 1
+    bits, vals = normal_bf16((M, ns * (hq + 2 * hkv) * dh), sigma, wid, 0)
+    return bits, vals
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dh,L,B", [(128, 200, 2), (128, 384, 1), (64, 130, 3)])
+def test_attention_mha(causal, dh, L, B):
+    heads, n = 8, 2
+    bits, q = qkv_case(B * L, heads, heads, dh, n, n, 2000 + dh + L)
+    note(f"attention mha dh={dh} L={L} B={B} causal={causal}")
+    got = host(tp.attention(bf16_tensor(bits), n, heads, heads, dh, L, causal))
+    ref = oracle.attention(q, n, heads, heads, dh, L, causal)
+    assert_close(got, ref, "attention", stored_bf16=True)
+
+
+@pytest.mark.parametrize("heads,kv_heads,n", [(8, 2, 4), (16, 4, 2), (8, 1, 8)])
+def test_attention_gqa(heads, kv_heads, n):
+    dh, L = 128, 256
+    bits, q = qkv_case(L, heads, kv_heads, dh, n, n, 2100 + heads + kv_heads + n)
+    note(f"attention gqa heads={heads} kv_heads={kv_heads} n={n}")
+    got = host(tp.attention(bf16_tensor(bits), n, heads, kv_heads, dh, L))
+    assert_close(got, oracle.attention(q, n, heads, kv_heads, dh, L), "attention gqa", stored_bf16=True)
+
+
+def test_attention_subset_partitioned_and_head_split():
+    heads, kv_heads, dh, L, n = 8, 4, 128, 320, 4
+    hq, hkv = 2, 1
+    # an unsharded QKV projection output, split into the shards' blocks by the head layout
+    fbits, full = normal_bf16((L, (heads + 2 * kv_heads) * dh), 1.0, 2200, 0)
+    cols = [oracle.shard_qkv_columns(heads, kv_heads, dh, n, s) for s in range(n)]
+    qkv_bits = np.concatenate([fbits[:, c] for c in cols], axis=1)
+    qkv_vals = np.concatenate([full[:, c] for c in cols], axis=1)
+    unsharded = oracle.attention_shard(full, heads, kv_heads, dh, L, True)
+    note("attention: all shards vs unsharded attention over all heads")
+    got = host(tp.attention(bf16_tensor(qkv_bits), n, heads, kv_heads, dh, L))
+    assert_close(got, unsharded, "all shards = unsharded", stored_bf16=True)
+    note("attention: shards 1..2 of 4, partitioned in and out")
+    blk = (hq + 2 * hkv) * dh
+    part = torch.stack([bf16_tensor(qkv_bits[:, s * blk:(s + 1) * blk]) for s in (1, 2)]).contiguous()
+    got = host(tp.attention(part, n, heads, kv_heads, dh, L, s0=1, ns=2, partitioned=True))
+    ref = oracle.attention(qkv_vals[:, blk:3 * blk], n, heads, kv_heads, dh, L, True, 1, 2)
+    assert_close(np.concatenate(list(got), axis=1), ref, "subset partitioned", stored_bf16=True)
+
+
+def test_attention_elementwise_path():
+    heads, n, L = 4, 2, 37
+    note("attention fp32 inputs (element-wise path)")
+    g = np.random.default_rng([2300, 0])
+    q = g.standard_normal((2 * L, 2 * (2 + 4) * 16)).astype(np.float32)
+    got = host(tp.attention(f32_tensor(q), n, heads, heads, 16, L))
+    assert_close(got, oracle.attention(q, n, heads, heads, 16, L), "fp32 attention")
+    note("attention bf16 head_dim 32 (element-wise path)")
+    bits, vals = qkv_case(3 * L, heads, 2, 32, n, n, 2301)
+    got = host(tp.attention(bf16_tensor(bits), n, heads, 2, 32, L, False))
+    assert_close(got, oracle.attention(vals, n, heads, 2, 32, L, False), "bf16 dh=32", stored_bf16=True)
+
+
+def test_attention_determinism():
+    bits, _ = qkv_case(512, 8, 8, 128, 2, 2, 2400)
+    x = bf16_tensor(bits)
+    note("attention determinism")
+    a = tp.attention(x, 2, 8, 8, 128, 512).clone()
+    b = tp.attention(x, 2, 8, 8, 128, 512).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_attention_projection_workload_full_shape():
+    # X [4096, 8192] -> QKV [4096, 24576] (8 shards of 8 heads x 128) -> attention over the
+    # 4096 tokens as one causal sequence; shards 0 and 7 are checked against the oracle
+    wl = WORKLOADS["attn_proj"]
+    heads, dh = 64, 128
+    xb, _ = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)
+    wb, _ = normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)
+    note("attention block: QKV projection then attention at full size")
+    qkv = tp.col_linear(bf16_tensor(xb), bf16_tensor(wb), wl.N)
+    out = host(tp.attention(qkv, wl.N, heads, heads, dh, wl.M))
+    qv = host(qkv)
+    blk = 3 * (heads // wl.N) * dh
+    oblk = (heads // wl.N) * dh
+    for s in (0, wl.N - 1):
+        ref = oracle.attention_shard(qv[:, s * blk:(s + 1) * blk], heads // wl.N, heads // wl.N, dh, wl.M, True)
+        assert_close(out[:, s * oblk:(s + 1) * oblk], ref, f"shard {s}", stored_bf16=True)
