@@ -34,7 +34,8 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth
 LEAD_CYCLES = 40_000_000  # ~20 ms of GPU spin at the ~2 GHz shader clock
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # Workloads that reuse the shapes of another one.
-BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp"}
+BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp", "attn_block": "attn_proj"}
+ATTN_HEADS, ATTN_HEAD_DIM = 64, 128  # the attention-projection workload: d = 8192 = 64 heads x 128
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
 # peak under "roofline"), with the decode-shaped MLP's HBM GB/s beside it.
 METRIC = "sharded-linear TFLOP/s (% of bf16 MFMA peak); decode-shape HBM GB/s"
@@ -95,6 +96,10 @@ def make_inputs(name, torch, dev):
         t["w1"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
         t["w2"] = up(normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)[0])
         t["dy"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 4)[0])
+    elif name == "attn_block":
+        t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
+        t["wqkv"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
+        t["wo"] = up(normal_bf16((wl.d, wl.out), 0.02, wl.wid, 2)[0])
     elif name == "decode_mlp":
         width = wl.F // wl.N
         t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
@@ -157,6 +162,34 @@ def plan(name, t, torch, tp):
             tp.col_linear(t["x"], t["wqkv"], wl.N, out=qkv)
             rec()
             tp.row_linear(t["a"], t["wo"], wl.N, out=p)
+            rec()
+            tp.reduce_partials(p, "rows", out=y)
+            rec()
+
+        return kernels, step
+    if name == "attn_block":
+        # QKV projection -> attention (the 4096 tokens as one causal sequence) -> W_o partials -> sum
+        qkv = torch.empty((wl.M, wl.F), dtype=torch.bfloat16, device=dev)
+        a = torch.empty((wl.M, wl.d), dtype=torch.bfloat16, device=dev)
+        p = torch.empty((wl.N, wl.M, wl.out), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.M, wl.out), dtype=torch.float32, device=dev)
+        pairs = wl.M * (wl.M + 1) / 2  # visible (query, key) pairs of one causal sequence
+        kernels = [
+            {"name": "qkv_col_gemm", "flop": flop(wl.M, wl.d, wl.F), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.d + wl.d * wl.F + wl.M * wl.F)},
+            {"name": "attention", "flop": 4.0 * ATTN_HEADS * ATTN_HEAD_DIM * pairs, "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.F + wl.M * wl.d)},
+            {"name": "wo_row_gemm_partials", "flop": flop(wl.M, wl.d, wl.out), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.d + wl.d * wl.out) + 4.0 * wl.N * wl.M * wl.out},
+            {"name": "reduce_partials", "flop": 0.0, "bound": "hbm", "bytes": 4.0 * (wl.N + 1) * wl.M * wl.out},
+        ]
+
+        def step(i, rec):
+            tp.col_linear(t["x"], t["wqkv"], wl.N, out=qkv)
+            rec()
+            tp.attention(qkv, wl.N, ATTN_HEADS, ATTN_HEADS, ATTN_HEAD_DIM, wl.M, True, out=a)
+            rec()
+            tp.row_linear(a, t["wo"], wl.N, out=p)
             rec()
             tp.reduce_partials(p, "rows", out=y)
             rec()
@@ -323,7 +356,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp",
-                             "megatron_mlp_bwd"])
+                             "megatron_mlp_bwd", "attn_block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for HBM counter calibration)")
@@ -344,7 +377,7 @@ def main():
     tp.library()  # fails loudly if the HIP library is missing
     main_name = "megatron_mlp" if args.workload in ("all", "megatron_mlp") else args.workload
     names = [main_name] if args.workload != "all" else ["megatron_mlp", "attn_proj", "gpt3_mlp_shard",
-                                                        "decode_mlp", "megatron_mlp_bwd"]
+                                                        "decode_mlp", "megatron_mlp_bwd", "attn_block"]
     results = {}
     for name in names:
         steps = args.steps if name in ("megatron_mlp", "decode_mlp") else max(3, args.steps // 5)

@@ -154,6 +154,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
 
   auto block = [&](int kb, const char* sk, const char* sv) {
     const int k0 = kb * BKV;
+    if (CAUSAL && k0 > qw + 31) return;  // every key of the block is past every query of this wave
     // S^T for 64 keys: tile kt covers keys 32 kt .. 32 kt + 31 of the block.
     f32x16 s[2];
 #pragma unroll
@@ -168,35 +169,52 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kt], 0, 0, 0);
       }
     }
-    // scale to log2 units and mask: element e of tile kt is key k0 + 32 kt + 8 (e / 4) + 4 hh + e % 4
+    // Mask (element e of tile kt is key k0 + 32 kt + 8 (e / 4) + 4 hh + e % 4) only
+    // where a key may lie past a query of this wave or past the sequence; the
+    // test is uniform across the wave, so other blocks skip it entirely.
+    const bool diag = CAUSAL && k0 + BKV - 1 > qw;
+    if (diag || k0 + BKV > L) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          if (key >= L || (CAUSAL && key > myq)) s[kt][e] = -INFINITY;
+        }
+    }
     float mloc = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
-        float v = s[kt][e] * c;
-        if (key >= L || (CAUSAL && key > myq)) v = -INFINITY;
-        s[kt][e] = v;
-        mloc = fmaxf(mloc, v);
-      }
+      for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kt][e]);
     const float mblk = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mblk);
-    // every query sees key 0 in the first block, so m_new is finite from then on
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    // Scores stay unscaled; the running max m is in score units and the scale
+    // c = log2(e) / sqrt(d) enters each exponent through one fused multiply-add.
+    // The reference m only moves when some query of the wave would otherwise
+    // see a probability above 2^8 (or on the first block): the softmax is
+    // unchanged by the choice of reference, so the rescale of O and l (and
+    // its exponential) is skipped for most blocks. Every query sees key 0 in
+    // the first block, so m is finite from then on.
+    const bool move = m_run == -INFINITY || (mblk - m_run) * c > 8.0f;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float m_new = fmaxf(m_run, mblk);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    }
+    const float mc = m_run * c;
     float lsum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(s[kt][e] - m_new);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, -mc));
         s[kt][e] = pv;
         lsum += pv;
       }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    l_run += lsum;
     // O^T += V^T P^T, 16 keys per step; step t takes elements 8 (t % 2) .. + 7 of tile t / 2,
     // i.e. keys 16 t + 8 (i / 4) + 4 hh + i % 4 for i = 0..7 (the k order of this step).
 #pragma unroll
