@@ -64,6 +64,10 @@ __all__ = [
     "attention_shard",
     "attention",
     "shard_qkv_columns",
+    "token_rows",
+    "layernorm",
+    "sp_layernorm",
+    "all_gather_rows",
 ]
 
 ACTS = ("none", "gelu")
@@ -397,3 +401,59 @@ def shard_qkv_columns(heads: int, kv_heads: int, head_dim: int, n: int, s: int) 
         for g in kv:
             cols += list(range((base + g) * head_dim, (base + g + 1) * head_dim))
     return np.array(cols)
+
+
+# ----------------------------------------------------------------------------- sequence parallelism
+#
+# [TP-topic] "Sequence Parallelism Extension": LayerNorm and Dropout are not
+# split by tensor parallelism, so the tokens are split over the shards for
+# them (each shard processes a subset of the tokens), with an all-gather
+# before attention (every token attends to every token) and a reduction after
+# it. On one device the all-reduce of the row-parallel partials splits into a
+# reduce-scatter (each token shard sums the partials of its own tokens, in
+# ascending shard order) and an all-gather (the token shards side by side
+# again). Readings: token shard s owns rows s*M/N .. (s+1)*M/N - 1; LayerNorm
+# normalizes each token over the hidden dimension with the biased variance,
+# (x - mean) / sqrt(var + eps) * gamma + beta; dropout is inverted dropout
+# with a caller-supplied 0/1 keep mask, applied to the reduced partials before
+# the residual is added (x = residual + keep * sum / (1 - p)).
+
+
+def token_rows(m: int, n: int, s: int) -> slice:
+    """The token rows of token shard s of n (contiguous, even split)."""
+    rows = _check_split(m, n, "tokens")
+    return slice(s * rows, (s + 1) * rows)
+
+
+def layernorm(x, gamma, beta, eps: float) -> np.ndarray:
+    """Per-row LayerNorm over the last dimension, float64, biased variance."""
+    x = widen(x)
+    mean = np.mean(x, axis=1, keepdims=True)
+    var = np.mean((x - mean) ** 2, axis=1, keepdims=True)
+    return (x - mean) / np.sqrt(var + eps) * widen(gamma)[None, :] + widen(beta)[None, :]
+
+
+def sp_layernorm(partials, residual, keep, p_drop: float, gamma, beta, eps: float, n: int, s0: int = 0,
+                 ns: int | None = None):
+    """Reduce-scatter, dropout, residual add and LayerNorm for the tokens of shards s0 .. s0+ns-1.
+
+    partials: the row-parallel fp32 partials [M, d] (a list, summed in order);
+    residual: [M, d] or None; keep: 0/1 [M, d] or None (no dropout).
+    Returns (x, y) for the executed token rows: x the pre-norm sum (the new
+    residual stream), y the normalized output.
+    """
+    ns = n - s0 if ns is None else ns
+    partials = list(partials)
+    m = widen(partials[0]).shape[0]
+    rows = slice(token_rows(m, n, s0).start, token_rows(m, n, s0 + ns - 1).stop)
+    x = reduce_sum([widen(pj)[rows] for pj in partials])
+    if keep is not None:
+        x = x * widen(keep)[rows] / (1.0 - p_drop)
+    if residual is not None:
+        x = x + widen(residual)[rows]
+    return x, layernorm(x, gamma, beta, eps)
+
+
+def all_gather_rows(blocks) -> np.ndarray:
+    """Token shards stacked back in order (the all-gather before attention)."""
+    return np.vstack([widen(b) for b in blocks])
