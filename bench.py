@@ -39,7 +39,7 @@ ATTN_HEADS, ATTN_HEAD_DIM = 64, 128  # the attention-projection workload: d = 81
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
 # peak under "roofline"), with the decode-shaped MLP's HBM GB/s beside it.
 METRIC = "sharded-linear TFLOP/s (% of bf16 MFMA peak); decode-shape HBM GB/s"
-KERNEL_SOURCES = ["gemm_mfma.hip", "gemm_skinny.hip", "combine.hip", "attention.hip"]
+KERNEL_SOURCES = ["gemm_mfma.hip", "gemm_skinny.hip", "combine.hip", "attention.hip", "sp_layernorm.hip"]
 
 
 def kernel_source_hash() -> str:

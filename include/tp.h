@@ -65,8 +65,11 @@ typedef enum tp_status {
 
 typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
 
-/* Which dimension of W is split: its output columns, or its rows (the contracted dimension). */
-typedef enum tp_axis { TP_SPLIT_COLS = 0, TP_SPLIT_ROWS = 1 } tp_axis;
+/*
+ * Which dimension is split: W's output columns, W's rows (the contracted
+ * dimension), or the token rows of the activations (sequence parallelism).
+ */
+typedef enum tp_axis { TP_SPLIT_COLS = 0, TP_SPLIT_ROWS = 1, TP_SPLIT_TOKENS = 2 } tp_axis;
 
 typedef enum tp_act { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_act;
 
@@ -135,15 +138,20 @@ tp_status tp_row_linear(const tp_matrix* X, const tp_matrix* W, int32_t N, int32
  * for the same coordinates are added, outputs for different coordinates are
  * concatenated; [TP-topic] "Tensor Parallelism Fundamentals").
  *   P     n blocks of [rows, cols] at ptr + j*shard_stride, row stride ld,
- *         dtype TP_F32 (axis ROWS) or TP_F32 / TP_BF16 (axis COLS).
+ *         dtype TP_F32 (axis ROWS) or TP_F32 / TP_BF16 (axis COLS, TOKENS).
  *   axis  TP_SPLIT_ROWS: the contracted dimension was split, so
  *           Y = P_0 + P_1 + ... + P_{n-1}, fp32, in ascending j
  *         (the single-GPU form of the all-reduce);
  *         TP_SPLIT_COLS: the output columns were split, so
- *           Y = [P_0 | P_1 | ... | P_{n-1}]  (Y.cols = n*cols; the all-gather).
- *   Y     [rows, cols] (ROWS) or [rows, n*cols] (COLS), dtype TP_F32 or
- *         TP_BF16 (ROWS: rounded from the fp32 sum; COLS: converted, exact
- *         when P and Y share a dtype), Y.shard_stride must be 0.
+ *           Y = [P_0 | P_1 | ... | P_{n-1}]  (Y.cols = n*cols; the all-gather);
+ *         TP_SPLIT_TOKENS: the token rows were split, so the blocks are
+ *           stacked in order, Y = [P_0; P_1; ...; P_{n-1}] (Y.rows = n*rows;
+ *           the all-gather of the token shards before attention, [TP-topic]
+ *           "Sequence Parallelism Extension").
+ *   Y     [rows, cols] (ROWS), [rows, n*cols] (COLS) or [n*rows, cols]
+ *         (TOKENS), dtype TP_F32 or TP_BF16 (ROWS: rounded from the fp32 sum;
+ *         COLS, TOKENS: converted, exact when P and Y share a dtype),
+ *         Y.shard_stride must be 0.
  */
 tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const tp_matrix* Y, void* stream);
 
@@ -264,6 +272,43 @@ tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matr
  */
 tp_status tp_attention(const tp_matrix* QKV, int32_t N, int32_t s0, int32_t ns, int32_t heads, int32_t kv_heads,
                        int32_t head_dim, int64_t seq_len, int32_t causal, const tp_matrix* A, void* stream);
+
+/*
+ * The sequence-parallel boundary after a row-parallel layer ([TP-topic]
+ * "Sequence Parallelism Extension": LayerNorm and dropout run on token
+ * shards, each shard holding M/N of the M tokens; the all-reduce of the
+ * row-parallel partials becomes a reduce-scatter, and an all-gather restores
+ * the full sequence before attention). For the tokens of shards
+ * s = s0 .. s0+ns-1 (token shard s owns rows s*M/N .. (s+1)*M/N - 1), with i
+ * the executed token row (i = 0 .. ns*M/N - 1, global row s0*M/N + i):
+ *     x_i  = R_i + keep_i * (P_0 + ... + P_{n-1})_i / (1 - p_drop)
+ *            (the reduce-scatter: the fp32 partial sum of this token slice
+ *             only, in ascending order; then dropout and the residual add)
+ *     X1_i = x_i                                  (the new residual stream)
+ *     Y_i  = (x_i - mean(x_i)) / sqrt(var(x_i) + eps) * gamma + beta
+ * with mean and var the mean and biased variance over the d features of the
+ * row, computed in fp32.
+ *   P      n blocks of [M, d], TP_F32, block t at ptr + t*shard_stride (the
+ *          output of tp_row_linear over all tokens); shard_stride may be 0
+ *          only when n = 1. N | M.
+ *   R      NULL (no residual) or logical [ns*M/N, d], TP_F32 or TP_BF16: the
+ *          residual rows of the executed token shards. shard_stride 0: one
+ *          matrix, token shard j at rows j*M/N; > 0: the [M/N, d] block of
+ *          token shard j at ptr + j*shard_stride.
+ *   keep   NULL (no dropout) or device bytes [ns*M/N, d], row stride d, each
+ *          0 (dropped) or 1 (kept); the mask is an input, drawn by the caller.
+ *   p_drop the drop probability, 0 <= p_drop < 1 (checked only with keep).
+ *   gamma, beta  device fp32 [d].  eps  >= 0.
+ *   X1     NULL or logical [ns*M/N, d], TP_F32, layout as R.
+ *   Y      logical [ns*M/N, d], TP_F32 or TP_BF16, layout as R.
+ * No output may overlap an input (an in-place residual update is rejected
+ * with TP_ERR_ALIAS). Rows of up to 16384 aligned features stay in registers
+ * (the partials are read once); wider or unaligned rows take a kernel that
+ * reads them three times.
+ */
+tp_status tp_sp_layernorm(const tp_matrix* P, int32_t n, const tp_matrix* R, const uint8_t* keep, float p_drop,
+                          const float* gamma, const float* beta, float eps, int32_t N, int32_t s0, int32_t ns,
+                          const tp_matrix* X1, const tp_matrix* Y, void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* tp_status_string(int32_t status);

@@ -11,7 +11,12 @@ Recipe (every workload):
   * floating inputs: ``standard_normal(float32) * sigma`` (sigma is the
     standard deviation: 1 for activations, 0.02 for weights), then rounded
     to bfloat16 by round-to-nearest-even; both sides receive these exact bits;
-  * integer inputs: ``integers(lo, hi + 1)`` stored as float32.
+  * integer inputs: ``integers(lo, hi + 1)`` stored as float32;
+  * sequence-parallel inputs (tensor ids 4 = residual, 5 = dropout keep
+    mask, 6 = LayerNorm gamma, 7 = beta): the residual as a floating input;
+    the keep mask as ``random() >= p_drop`` stored as 0/1 bytes (the random
+    numbers dropout draws are an input, passed to both sides); gamma and
+    beta as ``mean + sigma * standard_normal(float32)`` in float32.
 Values are dense and unstructured (no sparsity), as in the dense layers the
 tensor-parallelism pages describe.
 """
@@ -27,6 +32,8 @@ __all__ = [
     "f32_from_bf16_bits",
     "normal_bf16",
     "int_uniform_f32",
+    "normal_f32",
+    "keep_mask",
     "Workload",
     "WORKLOADS",
     "sample_rows",
@@ -67,6 +74,18 @@ def int_uniform_f32(shape, lo: int, hi: int, workload_id: int, tensor_id: int) -
     """Integers drawn uniformly from lo..hi inclusive, stored as float32."""
     g = rng(workload_id, tensor_id)
     return g.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def normal_f32(shape, mean: float, sigma: float, workload_id: int, tensor_id: int) -> np.ndarray:
+    """float32 draws mean + sigma * N(0, 1) (not rounded to bfloat16)."""
+    g = rng(workload_id, tensor_id)
+    return (np.float32(mean) + np.float32(sigma) * g.standard_normal(size=shape, dtype=np.float32)).astype(np.float32)
+
+
+def keep_mask(shape, p_drop: float, workload_id: int, tensor_id: int) -> np.ndarray:
+    """A dropout keep mask: uint8 1 where a uniform draw in [0, 1) is >= p_drop, else 0."""
+    g = rng(workload_id, tensor_id)
+    return (g.random(size=shape) >= p_drop).astype(np.uint8)
 
 
 def sample_rows(m: int, count: int = 256, seed: int = 0) -> np.ndarray:

@@ -17,8 +17,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (TP_ACT_GELU, TP_ACT_NONE, TP_BF16, TP_F32, TP_SPLIT_COLS, TP_SPLIT_ROWS, TpError,
-                   TpMatrix, status_string)
+from ._lib import (TP_ACT_GELU, TP_ACT_NONE, TP_BF16, TP_F32, TP_SPLIT_COLS, TP_SPLIT_ROWS, TP_SPLIT_TOKENS,
+                   TpError, TpMatrix, status_string)
 
 __all__ = [
     "col_linear",
@@ -31,13 +31,14 @@ __all__ = [
     "mlp_backward",
     "mlp_backward_workspace_bytes",
     "attention",
+    "sp_layernorm",
     "TpError",
     "library",
     "version",
 ]
 
 _ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU}
-_AXES = {"rows": TP_SPLIT_ROWS, "cols": TP_SPLIT_COLS}
+_AXES = {"rows": TP_SPLIT_ROWS, "cols": TP_SPLIT_COLS, "tokens": TP_SPLIT_TOKENS}
 
 
 def library() -> ctypes.CDLL:
@@ -155,11 +156,13 @@ def row_linear(x: torch.Tensor, w: torch.Tensor, n: int, s0: int = 0, ns: int | 
 
 def reduce_partials(p: torch.Tensor, axis: str = "rows", out: torch.Tensor | None = None,
                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """Combine shard outputs p [n, R, C]: sum (axis="rows") or concatenation (axis="cols")."""
+    """Combine shard outputs p [n, R, C]: sum (axis="rows"), concatenation of columns (axis="cols")
+    or token shards stacked in order (axis="tokens", [n*R, C])."""
     _require_gpu(p)
     n, r, c = p.shape
     if out is None:
-        out = torch.empty((r, c if axis == "rows" else n * c), dtype=out_dtype, device=p.device)
+        shape = {"rows": (r, c), "cols": (r, n * c), "tokens": (n * r, c)}[axis]
+        out = torch.empty(shape, dtype=out_dtype, device=p.device)
     _require_gpu(out)
     pm = _lib.matrix(p.data_ptr(), _dtype_code(p), r, c, max(p.stride(1), c), p.stride(0) if n > 1 else 0)
     ym = _full(out)
@@ -379,3 +382,55 @@ def attention(qkv: torch.Tensor, n: int, heads: int, kv_heads: int, head_dim: in
                                 ctypes.byref(am), ctypes.c_void_p(_stream(qkv)))
     _lib.check(st, "tp_attention")
     return out
+
+
+# ----------------------------------------------------------------------------- sequence parallelism
+
+
+def sp_layernorm(p: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, n: int, s0: int = 0,
+                 ns: int | None = None, residual: torch.Tensor | None = None, keep: torch.Tensor | None = None,
+                 p_drop: float = 0.0, eps: float = 1e-5, out: torch.Tensor | None = None,
+                 out_dtype: torch.dtype | None = None, residual_out: bool | torch.Tensor = False,
+                 partitioned: bool = False):
+    """Reduce-scatter, dropout, residual add and LayerNorm on token shards s0 .. s0+ns-1 (tp_sp_layernorm).
+
+    p: fp32 partials [t, M, d] (row_linear's output; summed in order) or [M, d].
+    residual, out, residual_out: [ns*M/n, d], or [ns, M/n, d] when partitioned.
+    keep: uint8 0/1 [ns*M/n, d] (contiguous), or None for no dropout.
+    Returns y, or (y, x) when residual_out is set (x = the pre-norm sum, fp32).
+    """
+    ns = n - s0 if ns is None else ns
+    p3 = p if p.dim() == 3 else p.unsqueeze(0)
+    _require_gpu(p3, gamma, beta)
+    t, m, d = p3.shape
+    rows = ns * (m // n) if n > 0 else 0
+    shape = (ns, rows // ns if ns > 0 else 0, d) if partitioned else (rows, d)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype or torch.float32, device=p.device)
+    x1 = None
+    if isinstance(residual_out, torch.Tensor):
+        x1 = residual_out
+    elif residual_out:
+        x1 = torch.empty(shape, dtype=torch.float32, device=p.device)
+    for a in (out, x1, residual):
+        if a is not None:
+            _require_gpu(a)
+    if keep is not None:
+        _require_gpu(keep)
+        if keep.dtype != torch.uint8 or not keep.is_contiguous() or keep.numel() != rows * d:
+            raise ValueError("keep must be a contiguous uint8 tensor of ns*M/n x d elements")
+    if not (gamma.dtype == beta.dtype == torch.float32 and gamma.is_contiguous() and beta.is_contiguous()):
+        raise ValueError("gamma and beta must be contiguous float32 vectors")
+    if gamma.numel() != d or beta.numel() != d:
+        raise ValueError(f"gamma and beta must hold {d} elements")
+    pm = _lib.matrix(p3.data_ptr(), _dtype_code(p3), m, d,
+                     max(p3.stride(1), d), p3.stride(0) if t > 1 else 0)
+    ym = _blocks(out, rows, d)
+    rm = _blocks(residual, rows, d) if residual is not None else None
+    xm = _blocks(x1, rows, d) if x1 is not None else None
+    st = library().tp_sp_layernorm(ctypes.byref(pm), t, _ref(rm),
+                                   ctypes.c_void_p(keep.data_ptr() if keep is not None else 0), float(p_drop),
+                                   ctypes.c_void_p(gamma.data_ptr()), ctypes.c_void_p(beta.data_ptr()), float(eps),
+                                   n, s0, ns, _ref(xm), ctypes.byref(ym), ctypes.c_void_p(_stream(p3)))
+    _lib.check(st, "tp_sp_layernorm")
+    return (out, x1) if x1 is not None else out

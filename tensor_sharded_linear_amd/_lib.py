@@ -26,7 +26,7 @@ STATUS_NAMES = {
     10: "TP_ERR_TOO_LARGE",
 }
 TP_F32, TP_BF16 = 0, 1
-TP_SPLIT_COLS, TP_SPLIT_ROWS = 0, 1
+TP_SPLIT_COLS, TP_SPLIT_ROWS, TP_SPLIT_TOKENS = 0, 1, 2
 TP_ACT_NONE, TP_ACT_GELU = 0, 1
 
 # Every function the header declares, with its ctypes signature.
@@ -39,6 +39,7 @@ EXPORTS = (
     "tp_row_linear_backward",
     "tp_mlp_backward",
     "tp_attention",
+    "tp_sp_layernorm",
     "tp_status_string",
     "tp_version",
 )
@@ -101,6 +102,10 @@ def load() -> ctypes.CDLL:
     lib.tp_attention.argtypes = [_M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _M, ctypes.c_void_p]
     lib.tp_attention.restype = ctypes.c_int32
+    lib.tp_sp_layernorm.argtypes = [_M, ctypes.c_int32, _M, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    _M, _M, ctypes.c_void_p]
+    lib.tp_sp_layernorm.restype = ctypes.c_int32
     lib.tp_status_string.argtypes = [ctypes.c_int32]
     lib.tp_status_string.restype = ctypes.c_char_p
     lib.tp_version.argtypes = []

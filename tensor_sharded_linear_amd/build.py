@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtp_amd.so")
 ARCH = os.environ.get("TP_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["tp_api.cpp", "gemm_mfma.hip", "gemm_skinny.hip", "gemm_generic.hip", "combine.hip", "attention.hip"]
+SOURCES = ["tp_api.cpp", "gemm_mfma.hip", "gemm_skinny.hip", "gemm_generic.hip", "combine.hip", "attention.hip",
+           "sp_layernorm.hip"]
 
 
 def hipcc() -> str:

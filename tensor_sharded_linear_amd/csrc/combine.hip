@@ -2,7 +2,9 @@
 //
 // Sum (the local form of the all-reduce): Y = P_0 + P_1 + ... + P_{n-1} in
 // fp32, added in ascending shard order so that every run gives the same bits.
-// Concatenation (the local form of the all-gather): Y = [P_0 | ... | P_{n-1}].
+// Concatenation (the local form of the all-gather): Y = [P_0 | ... | P_{n-1}],
+// or the blocks stacked by rows (token shards gathered back in order, the
+// all-gather of sequence parallelism).
 // The rule for choosing between them is the one of the "Tensor Parallelism"
 // entry of the AI Glossary (aiforbusinessandlife.com), "Check your
 // understanding": partial results for the same output coordinates are added,
@@ -80,7 +82,8 @@ __global__ __launch_bounds__(256) void concat_kernel(CombineDesc d) {
     const int64_t r = rem / d.cols, c = rem - r * d.cols;
     const int64_t src = j * d.sP + r * d.ldp + c;
     const float v = PBF16 ? (float)static_cast<const __bf16*>(d.P)[src] : static_cast<const float*>(d.P)[src];
-    const int64_t dst = r * d.ldy + j * d.cols + c;
+    // concat 1: blocks side by side (columns); 2: stacked (rows)
+    const int64_t dst = d.concat == 2 ? (j * d.rows + r) * d.ldy + c : r * d.ldy + j * d.cols + c;
     if (YBF16) static_cast<__bf16*>(d.Y)[dst] = (__bf16)v;
     else static_cast<float*>(d.Y)[dst] = v;
   }

@@ -44,6 +44,8 @@ bool overlaps(const Range& a, const Range& b) {
 
 // Sizes beyond these would overflow the kernels' 32-bit tile and grid arithmetic.
 constexpr int64_t kMaxDim = (1ll << 31) - 1;
+// One 256-thread workgroup per token row; a launch holds fewer than 2^32 work-items.
+constexpr int64_t kMaxLnRows = (1ll << 24) - 1;
 
 // Checks one matrix holding `nblocks` blocks of [brows, bcols]:
 //   shard_stride == 0 -> the blocks are slices of one matrix whose rows need
@@ -297,19 +299,21 @@ tp_status tp_row_linear(const tp_matrix* X, const tp_matrix* W, int32_t N, int32
 tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const tp_matrix* Y, void* stream) {
   if (!P || !Y) return TP_ERR_NULL;
   if (!valid_dtype(P->dtype) || !valid_dtype(Y->dtype)) return TP_ERR_DTYPE;
-  if (axis != TP_SPLIT_ROWS && axis != TP_SPLIT_COLS) return TP_ERR_SHAPE;
+  if (axis != TP_SPLIT_ROWS && axis != TP_SPLIT_COLS && axis != TP_SPLIT_TOKENS) return TP_ERR_SHAPE;
   if (axis == TP_SPLIT_ROWS && P->dtype != TP_F32) return TP_ERR_DTYPE;
   if (n < 1) return TP_ERR_INDIVISIBLE;
   if (P->rows < 0 || P->cols < 0 || Y->rows < 0 || Y->cols < 0) return TP_ERR_SHAPE;
   const int64_t R = P->rows, C = P->cols;
-  const int64_t ycols = axis == TP_SPLIT_ROWS ? C : (int64_t)n * C;
-  if (Y->rows != R || Y->cols != ycols) return TP_ERR_SHAPE;
+  const int64_t ycols = axis == TP_SPLIT_COLS ? (int64_t)n * C : C;
+  const int64_t yrows = axis == TP_SPLIT_TOKENS ? (int64_t)n * R : R;
+  if (Y->rows != yrows || Y->cols != ycols) return TP_ERR_SHAPE;
+  if (yrows > kMaxDim || ycols > kMaxDim) return TP_ERR_TOO_LARGE;
   if (Y->shard_stride != 0) return TP_ERR_STRIDE;
   if (n > 1 && P->shard_stride == 0 && R > 0 && C > 0) return TP_ERR_STRIDE;
   tp_status st;
   if ((st = check_matrix(P, n, R, C, C)) != TP_OK) return st;
-  if ((st = check_matrix(Y, 1, R, ycols, ycols)) != TP_OK) return st;
-  if (overlaps(range_of(Y->ptr, Y->dtype, 1, 0, R, ycols, Y->ld),
+  if ((st = check_matrix(Y, 1, yrows, ycols, ycols)) != TP_OK) return st;
+  if (overlaps(range_of(Y->ptr, Y->dtype, 1, 0, yrows, ycols, Y->ld),
                range_of(P->ptr, P->dtype, n, P->shard_stride, R, C, P->ld)))
     return TP_ERR_ALIAS;
   CombineDesc d;
@@ -324,8 +328,92 @@ tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const 
   d.n = n;
   d.p_bf16 = P->dtype == TP_BF16;
   d.y_bf16 = Y->dtype == TP_BF16;
-  d.concat = axis == TP_SPLIT_COLS;
+  d.concat = axis == TP_SPLIT_COLS ? 1 : axis == TP_SPLIT_TOKENS ? 2 : 0;
   return hip_status(tp::launch_combine(d, static_cast<hipStream_t>(stream)));
+}
+
+tp_status tp_sp_layernorm(const tp_matrix* P, int32_t n, const tp_matrix* R, const uint8_t* keep, float p_drop,
+                          const float* gamma, const float* beta, float eps, int32_t N, int32_t s0, int32_t ns,
+                          const tp_matrix* X1, const tp_matrix* Y, void* stream) {
+  if (!P || !Y) return TP_ERR_NULL;
+  if (P->dtype != TP_F32 || !valid_dtype(Y->dtype)) return TP_ERR_DTYPE;
+  if (R && !valid_dtype(R->dtype)) return TP_ERR_DTYPE;
+  if (X1 && X1->dtype != TP_F32) return TP_ERR_DTYPE;
+  if (P->rows < 0 || P->cols < 0 || Y->rows < 0 || Y->cols < 0) return TP_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_SHAPE;
+  if (keep && !(p_drop >= 0.0f && p_drop < 1.0f)) return TP_ERR_SHAPE;
+  if (n < 1 || N < 1) return TP_ERR_INDIVISIBLE;
+  if (s0 < 0 || ns < 1 || (int64_t)s0 + ns > N) return TP_ERR_SHARD_RANGE;
+  const int64_t M = P->rows, D = P->cols;
+  if (M % N != 0) return TP_ERR_INDIVISIBLE;
+  const int64_t T = M / N, rows = (int64_t)ns * T;
+  if (Y->rows != rows || Y->cols != D) return TP_ERR_SHAPE;
+  if (R && (R->rows != rows || R->cols != D)) return TP_ERR_SHAPE;
+  if (X1 && (X1->rows != rows || X1->cols != D)) return TP_ERR_SHAPE;
+  if (n > 1 && P->shard_stride == 0 && M > 0 && D > 0) return TP_ERR_STRIDE;
+  tp_status st;
+  if ((st = check_matrix(P, n, M, D, D)) != TP_OK) return st;
+  if ((st = check_matrix(Y, ns, T, D, D)) != TP_OK) return st;
+  if (R && (st = check_matrix(R, ns, T, D, D)) != TP_OK) return st;
+  if (X1 && (st = check_matrix(X1, ns, T, D, D)) != TP_OK) return st;
+  if (rows == 0 || D == 0) return TP_OK;
+  if (!gamma || !beta) return TP_ERR_NULL;
+  if (rows > kMaxLnRows) return TP_ERR_TOO_LARGE;
+  const Blocks pb = row_blocks(P, 0, M), yb = row_blocks(Y, 0, T);
+  const Range ry = blocks_range(yb, ns, T, D);
+  Range inputs[5] = {blocks_range(pb, n, M, D)};
+  Blocks rb{}, xb{};
+  if (R) {
+    rb = row_blocks(R, 0, T);
+    inputs[1] = blocks_range(rb, ns, T, D);
+  }
+  if (keep) {
+    inputs[2].lo = reinterpret_cast<uintptr_t>(keep);
+    inputs[2].hi = inputs[2].lo + (uintptr_t)(rows * D);
+  }
+  inputs[3].lo = reinterpret_cast<uintptr_t>(gamma);
+  inputs[3].hi = inputs[3].lo + (uintptr_t)(D * 4);
+  inputs[4].lo = reinterpret_cast<uintptr_t>(beta);
+  inputs[4].hi = inputs[4].lo + (uintptr_t)(D * 4);
+  Range rx;
+  if (X1) {
+    xb = row_blocks(X1, 0, T);
+    rx = blocks_range(xb, ns, T, D);
+    if (overlaps(rx, ry)) return TP_ERR_ALIAS;
+  }
+  for (const Range& in : inputs)
+    if (overlaps(ry, in) || overlaps(rx, in)) return TP_ERR_ALIAS;
+  tp::LnDesc d;
+  std::memset(&d, 0, sizeof(d));
+  // the partials' rows of the executed tokens, block t at t * shard_stride
+  d.P = reinterpret_cast<const float*>(pb.base) + (int64_t)s0 * T * P->ld;
+  d.ldp = P->ld;
+  d.sP = P->shard_stride;
+  d.n = n;
+  if (R) {
+    d.R = rb.base;
+    d.ldr = rb.ld;
+    d.sR = rb.step;
+    d.r_bf16 = R->dtype == TP_BF16;
+  }
+  d.keep = keep;
+  d.keep_scale = keep ? 1.0f / (1.0f - p_drop) : 1.0f;
+  d.gamma = gamma;
+  d.beta = beta;
+  d.eps = eps;
+  if (X1) {
+    d.X1 = reinterpret_cast<float*>(const_cast<char*>(xb.base));
+    d.ldx1 = xb.ld;
+    d.sX1 = xb.step;
+  }
+  d.Y = const_cast<char*>(yb.base);
+  d.ldy = yb.ld;
+  d.sY = yb.step;
+  d.y_bf16 = Y->dtype == TP_BF16;
+  d.rows_per_shard = T;
+  d.rows = rows;
+  d.cols = D;
+  return hip_status(tp::launch_sp_layernorm(d, static_cast<hipStream_t>(stream)));
 }
 
 tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, int32_t N, int32_t s0, int32_t ns,

@@ -52,7 +52,7 @@ struct CombineDesc {
   int32_t n;
   int32_t p_bf16;    // P dtype (COLS mode only)
   int32_t y_bf16;    // Y dtype
-  int32_t concat;    // 1: Y = [P_0 | ... | P_{n-1}], 0: Y = sum
+  int32_t concat;    // 0: Y = sum; 1: Y = [P_0 | ... | P_{n-1}]; 2: Y = the blocks stacked by rows
 };
 
 // GeLU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, applied to the fp32
@@ -119,6 +119,34 @@ hipError_t launch_skinny_finish(const GemmDesc& d, int ksplit, const float* part
 hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t stream);
 
 hipError_t launch_combine(const CombineDesc& d, hipStream_t stream);
+
+// Sequence-parallel LayerNorm over token rows (see tp_sp_layernorm). Row i of
+// the executed token rows (token shard j = i / rows_per_shard, row
+// r = i % rows_per_shard within it): x = R_j[r] + keep[i] * sum_{t<n} P_t[i]
+// * keep_scale (keep and R optional), X1_j[r] = x (optional), Y_j[r] =
+// (x - mean) / sqrt(var + eps) * gamma + beta. P_t[i] is P + t * sP + i * ldp;
+// the per-shard matrices R, X1 and Y hold shard j at j * s elements.
+struct LnDesc {
+  const float* P;
+  int64_t ldp, sP;
+  int32_t n;
+  const void* R;
+  int64_t ldr, sR;
+  int32_t r_bf16;
+  const uint8_t* keep;  // [rows, cols] 0/1 bytes, row stride cols
+  float keep_scale;     // 1 / (1 - p)
+  const float* gamma;
+  const float* beta;
+  float eps;
+  float* X1;
+  int64_t ldx1, sX1;
+  void* Y;
+  int64_t ldy, sY;
+  int32_t y_bf16;
+  int64_t rows_per_shard;
+  int64_t rows, cols;
+};
+hipError_t launch_sp_layernorm(const LnDesc& d, hipStream_t stream);
 
 // Attention over the heads of `shards` executed shards (see tp_attention):
 // shard j's QKV block [tokens, (hq + 2 hkv) head_dim] starts s_qkv elements

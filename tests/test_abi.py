@@ -277,3 +277,47 @@ def test_attention_validation(lib):
     assert att(Q, 2, 1, 2, 8, 8, 16, 10, 1, A) == 5
     assert att(Q, 2, 0, 2, 8, 8, 16, 10, 1, m(FAKE + 64, rows=20, cols=128)) == 7  # output over QKV
     assert att(Q, 2, 0, 2, 8, 8, 16, 10, 1, m(FAKE + (1 << 20), rows=20, cols=128, ld=100)) == 6
+
+
+def test_reduce_tokens_axis_validation(lib):
+    P = m(FAKE, dtype=BF16, rows=4, cols=16, stride=64)
+    red = lib.tp_reduce_partials
+    assert red(ctypes.byref(P), 2, 2, ctypes.byref(m(FAKE + (1 << 20), dtype=F32, rows=4, cols=16)), None) == 3
+    assert red(ctypes.byref(P), 2, 2, ctypes.byref(m(FAKE + (1 << 20), dtype=F32, rows=8, cols=32)), None) == 3
+    assert red(ctypes.byref(P), 2, 2, ctypes.byref(m(FAKE + 16, dtype=BF16, rows=8, cols=16)), None) == 7
+    assert red(ctypes.byref(P), 2, 2, ctypes.byref(m(FAKE + (1 << 20), dtype=F32, rows=8, cols=16, ld=8)),
+               None) == 6
+
+
+def test_sp_layernorm_validation(lib):
+    # 2 partials of [8 tokens, 16] over N = 4 token shards (2 tokens each); shards 1..2 -> 4 rows
+    def ln(P, n, R, keep, p, g, b, eps, N, s0, ns, X1, Y):
+        r = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+        return lib.tp_sp_layernorm(r(P), n, r(R), keep, p, g, b, eps, N, s0, ns, r(X1), r(Y), None)
+
+    G, B = FAKE + (3 << 20), FAKE + (3 << 20) + 64
+    P = m(FAKE, dtype=F32, rows=8, cols=16, stride=128)
+    Y = m(FAKE + (1 << 20), dtype=BF16, rows=4, cols=16)
+    R = m(FAKE + (2 << 20), dtype=BF16, rows=4, cols=16)
+    X1 = m(FAKE + (4 << 20), dtype=F32, rows=4, cols=16)
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, X1, None) == 1
+    assert ln(P, 2, R, None, 0.0, None, B, 1e-5, 4, 1, 2, X1, Y) == 1         # gamma missing
+    assert ln(m(FAKE, rows=8, cols=16, stride=128), 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, X1, Y) == 2
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, m(FAKE + (4 << 20), rows=4, cols=16), Y) == 2
+    assert ln(P, 2, R, None, 0.0, G, B, -1.0, 4, 1, 2, X1, Y) == 3           # eps < 0
+    assert ln(P, 2, R, FAKE + (5 << 20), 1.0, G, B, 1e-5, 4, 1, 2, X1, Y) == 3  # p_drop = 1
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 4, X1, Y) == 5
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 3, 0, 1, X1, Y) == 4           # 3 does not split 8 tokens
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 1, X1, Y) == 3           # Y holds 2 shards' rows
+    assert ln(P, 2, m(FAKE + (2 << 20), rows=4, cols=8), None, 0.0, G, B, 1e-5, 4, 1, 2, X1, Y) == 3
+    assert ln(m(FAKE, dtype=F32, rows=8, cols=16), 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, X1, Y) == 6
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, X1, m(FAKE + (1 << 20), dtype=BF16, rows=4, cols=16,
+                                                                  ld=8)) == 6
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, X1, m(FAKE + 64, dtype=F32, rows=4, cols=16)) == 7
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, m(FAKE + (2 << 20), dtype=F32, rows=4, cols=16), Y) == 7
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, X1, m(G - 32, dtype=F32, rows=4, cols=16)) == 7
+    assert ln(P, 2, R, None, 0.0, G, B, 1e-5, 4, 1, 2, X1, m(FAKE + (4 << 20) + 64, dtype=F32, rows=4,
+                                                               cols=16)) == 7  # Y over X1
+    # nothing to do: zero tokens
+    assert ln(m(FAKE, dtype=F32, rows=0, cols=16, stride=128), 2, None, None, 0.0, None, None, 1e-5, 4, 1, 2,
+              None, m(FAKE + (1 << 20), dtype=BF16, rows=0, cols=16)) == 0
