@@ -34,7 +34,8 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth
 LEAD_CYCLES = 40_000_000  # ~20 ms of GPU spin at the ~2 GHz shader clock
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # Workloads that reuse the shapes of another one.
-BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp", "attn_block": "attn_proj"}
+BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp", "attn_block": "attn_proj", "mlp_sp_block": "megatron_mlp"}
+SP_P_DROP = 0.1
 ATTN_HEADS, ATTN_HEAD_DIM = 64, 128  # the attention-projection workload: d = 8192 = 64 heads x 128
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
 # peak under "roofline"), with the decode-shaped MLP's HBM GB/s beside it.
@@ -96,6 +97,14 @@ def make_inputs(name, torch, dev):
         t["w1"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
         t["w2"] = up(normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)[0])
         t["dy"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 4)[0])
+    elif name == "mlp_sp_block":
+        from synthetic import keep_mask, normal_f32
+        t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
+        t["w1"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
+        t["w2"] = up(normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)[0])
+        t["keep"] = torch.from_numpy(keep_mask((wl.M, wl.d), SP_P_DROP, wl.wid, 5)).to(dev)
+        t["gamma"] = torch.from_numpy(normal_f32((wl.d,), 1.0, 0.1, wl.wid, 6)).to(dev)
+        t["beta"] = torch.from_numpy(normal_f32((wl.d,), 0.0, 0.1, wl.wid, 7)).to(dev)
     elif name == "attn_block":
         t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
         t["wqkv"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
@@ -192,6 +201,35 @@ def plan(name, t, torch, tp):
             tp.row_linear(a, t["wo"], wl.N, out=p)
             rec()
             tp.reduce_partials(p, "rows", out=y)
+            rec()
+
+        return kernels, step
+    if name == "mlp_sp_block":
+        # the MLP pair, then the sequence-parallel boundary: reduce-scatter of the partials over the 8
+        # token shards, dropout, residual add, LayerNorm (the token shards' outputs land in one matrix,
+        # so the all-gather that follows is the identity in memory)
+        width = wl.F // wl.N
+        h = torch.empty((wl.N, wl.M, width), dtype=torch.bfloat16, device=dev)
+        p = torch.empty((wl.N, wl.M, wl.d), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.M, wl.d), dtype=torch.bfloat16, device=dev)
+        x1 = torch.empty((wl.M, wl.d), dtype=torch.float32, device=dev)
+        kernels = [
+            {"name": "col_gemm_gelu", "flop": flop(wl.M, wl.d, wl.F), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.d + wl.d * wl.F + wl.M * wl.F)},
+            {"name": "row_gemm_partials", "flop": flop(wl.M, wl.F, wl.d), "bound": "mfma",
+             "bytes": 2.0 * (wl.M * wl.F + wl.F * wl.d) + 4.0 * wl.N * wl.M * wl.d},
+            # partials in, keep bytes, bf16 residual, fp32 pre-norm sum and bf16 output out
+            {"name": "sp_layernorm", "flop": 0.0, "bound": "hbm",
+             "bytes": (4.0 * wl.N + 1 + 2 + 4 + 2) * wl.M * wl.d + 8.0 * wl.d},
+        ]
+
+        def step(i, rec):
+            tp.col_linear(t["x"], t["w1"], wl.N, act="gelu", out=h, partitioned=True)
+            rec()
+            tp.row_linear(h, t["w2"], wl.N, out=p)
+            rec()
+            tp.sp_layernorm(p, t["gamma"], t["beta"], wl.N, residual=t["x"], keep=t["keep"], p_drop=SP_P_DROP,
+                            out=y, residual_out=x1)
             rec()
 
         return kernels, step
@@ -356,7 +394,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp",
-                             "megatron_mlp_bwd", "attn_block"])
+                             "megatron_mlp_bwd", "attn_block", "mlp_sp_block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for HBM counter calibration)")
@@ -377,7 +415,8 @@ def main():
     tp.library()  # fails loudly if the HIP library is missing
     main_name = "megatron_mlp" if args.workload in ("all", "megatron_mlp") else args.workload
     names = [main_name] if args.workload != "all" else ["megatron_mlp", "attn_proj", "gpt3_mlp_shard",
-                                                        "decode_mlp", "megatron_mlp_bwd", "attn_block"]
+                                                        "decode_mlp", "megatron_mlp_bwd", "attn_block",
+                                                        "mlp_sp_block"]
     results = {}
     for name in names:
         steps = args.steps if name in ("megatron_mlp", "decode_mlp") else max(3, args.steps // 5)
