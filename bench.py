@@ -307,11 +307,13 @@ def time_workload(name, steps, warmup, torch, tp):
     per_kernel = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(nk)] for i in range(steps)])
     step_ms = np.array([ev[i][0].elapsed_time(ev[i][nk]) for i in range(steps)])
     res = {"workload": name, "steps": steps, "ms_per_step": float(step_ms.mean()),
-           "ms_per_step_min": float(step_ms.min()), "wall_s": wall, "kernels": []}
+           "ms_per_step_median": float(np.median(step_ms)), "ms_per_step_min": float(step_ms.min()),
+           "wall_s": wall, "kernels": []}
     total_flop = sum(k["flop"] for k in kernels)
     for j, k in enumerate(kernels):
         ms = float(per_kernel[:, j].mean())
-        entry = {"name": k["name"], "ms": ms, "ms_min": float(per_kernel[:, j].min()), "bound": k["bound"]}
+        entry = {"name": k["name"], "ms": ms, "ms_median": float(np.median(per_kernel[:, j])),
+                 "ms_min": float(per_kernel[:, j].min()), "bound": k["bound"]}
         if k["flop"]:
             entry["tflops"] = k["flop"] / (ms * 1e-3) / 1e12
             entry["frac_mfma_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
@@ -324,6 +326,19 @@ def time_workload(name, steps, warmup, torch, tp):
         res["gbs"] = res["alg_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
     res["_kernels_def"] = kernels
     return res
+
+
+def engine_clock_mhz():
+    """The current engine clock level the driver reports (sysfs, read-only), or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
 
 
 def roofline_for(res):
@@ -390,7 +405,7 @@ def copy_calibration(torch, gib: float = 1.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp",
@@ -422,6 +437,7 @@ def main():
         steps = args.steps if name in ("megatron_mlp", "decode_mlp") else max(3, args.steps // 5)
         print(f"[bench] {name}: warmup {args.warmup}, steps {steps}", file=sys.stderr, flush=True)
         results[name] = time_workload(name, steps, args.warmup, torch, tp)
+        results[name]["sclk_mhz_after"] = engine_clock_mhz()
         torch.cuda.empty_cache()
         print(f"[bench] {name}: {results[name]['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
 
@@ -451,6 +467,8 @@ def main():
                    "parallelism": f"tp{wl.N} shards executed on 1 GPU"},
         "frac_of_bf16_peak": (main["tflops"] / PEAK_BF16_TFLOPS) if main_name != "decode_mlp" else None,
         "roofline": roofline_for(main),
+        "ms_per_step_median": main["ms_per_step_median"],
+        "sclk_mhz_after": main["sclk_mhz_after"],
         "kernels": main["kernels"],
     }
     secondary = []
