@@ -165,7 +165,7 @@ struct Frags {
   }
 };
 
-template <int OUT, int ACT, bool AT, bool BT>
+template <int OUT, int ACT, bool AT, bool BT, bool WEAVE>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
   // Two stages of A and B, each its own array so the compiler can tell the
   // stage being filled by LDS-mode loads from the stage being read.
@@ -226,6 +226,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
 
   Frags<A_KROWS, FM> ra;
   Frags<B_KROWS, FN> rb;
+  // LDS reads per 16-wide k step: one b128 per K-rows fragment, two transpose reads per MN-rows one
+  constexpr int kReads = (A_KROWS ? FM : 2 * FM) + (B_KROWS ? FN : 2 * FN);
   ra.init(lane, wm * WM);
   rb.init(lane, wn * WN);
   bf16x8 fa[2][FM], fb[2][FN];
@@ -255,6 +257,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn)
           acc[im][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][im], fb[kk & 1][jn], acc[im][jn], 0, 0, 0);
+      // WEAVE: interleave the next step's fragment reads with this step's
+      // MFMAs, two MFMAs at a time, so every read has MFMAs to hide behind
+      // (left alone, the compiler issues each read right before the MFMA that
+      // needs it). Measured 3-6% faster for K up to 6144, 1-3% slower for
+      // K of 8192 and more, where the kernels run long enough for the
+      // engine clock to settle lower under the busier matrix cores.
+      if (WEAVE && kk + 1 < BK / 16) {
+        constexpr int r0 = kReads / 4, r1 = kReads * 2 / 4 - r0, r2 = kReads * 3 / 4 - r0 - r1;
+        constexpr int r3 = kReads - r0 - r1 - r2, m = FM * FN / 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, r0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, r1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, r2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, r3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+      }
     }
     __syncthreads();
     if (kt + 1 < KT) read_frags(na, nb, 0, 0);
@@ -324,9 +344,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
   }
 }
 
+constexpr int64_t kWeaveMaxK = 6144;
+
 template <int OUT, int ACT, bool AT, bool BT>
 void launch_one(const Params& p, hipStream_t s) {
-  gemm_bf16_mfma_kernel<OUT, ACT, AT, BT><<<dim3((unsigned)p.total), dim3(NTHREADS), 0, s>>>(p);
+  if (p.d.K <= kWeaveMaxK)
+    gemm_bf16_mfma_kernel<OUT, ACT, AT, BT, true><<<dim3((unsigned)p.total), dim3(NTHREADS), 0, s>>>(p);
+  else
+    gemm_bf16_mfma_kernel<OUT, ACT, AT, BT, false><<<dim3((unsigned)p.total), dim3(NTHREADS), 0, s>>>(p);
 }
 
 }  // namespace
