@@ -313,7 +313,7 @@ tp_status tp_sp_layernorm(const tp_matrix* P, int32_t n, const tp_matrix* R, con
 /* A static, human-readable name for a status code (never NULL). */
 const char* tp_status_string(int32_t status);
 
-/* Version of this interface: (major << 16) | minor. */
+/* Version of this interface: (major << 16) | minor. 1.1 added tp_sp_layernorm and TP_SPLIT_TOKENS. */
 int32_t tp_version(void);
 
 #ifdef __cplusplus

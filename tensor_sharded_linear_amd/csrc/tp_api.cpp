@@ -862,6 +862,6 @@ const char* tp_status_string(int32_t status) {
   }
 }
 
-int32_t tp_version(void) { return (1 << 16) | 0; }
+int32_t tp_version(void) { return (1 << 16) | 1; }  // 1.1: sequence-parallel LayerNorm, token stacking
 
 }  // extern "C"

@@ -44,6 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.tp_version() >> 16 == 1
+    assert lib.tp_version() & 0xffff >= 1  # tp_sp_layernorm and TP_SPLIT_TOKENS
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode().startswith(name)
     assert lib.tp_status_string(999).decode() == "unknown tp_status"
