@@ -170,12 +170,13 @@ def _variant(scale=True, diag_masked=False, swap_kv=False, mod_group=False, igno
                 s = q @ k.T / (np.sqrt(head_dim) if scale else 1.0)
                 if causal:
                     s = np.where(np.tril(np.ones((L, L), dtype=bool), -1 if diag_masked else 0), s, -np.inf)
-                if col_softmax:
-                    e = np.exp(s - np.max(s, axis=0, keepdims=True))
-                    p = e / np.sum(e, axis=0, keepdims=True)
-                else:
-                    e = np.exp(s - np.max(s, axis=1, keepdims=True))
-                    p = e / np.sum(e, axis=1, keepdims=True)
+                with np.errstate(invalid="ignore"):  # a planted mask can leave a row with no key
+                    if col_softmax:
+                        e = np.exp(s - np.max(s, axis=0, keepdims=True))
+                        p = e / np.sum(e, axis=0, keepdims=True)
+                    else:
+                        e = np.exp(s - np.max(s, axis=1, keepdims=True))
+                        p = e / np.sum(e, axis=1, keepdims=True)
                 out[rows, h * head_dim:(h + 1) * head_dim] = np.nan_to_num(p) @ v
         return out
 
