@@ -181,3 +181,29 @@ def test_megatron_mlp_then_sp_layernorm_full_size():
     rx, ry = oracle.sp_layernorm(parts, x[rows], keep[rows], 0.1, gamma, beta, EPS, 1)
     assert_close(xh[rows], rx, "pre-norm sum, sampled rows")
     assert_close(yh[rows], ry, "LayerNorm output, sampled rows", stored_bf16=True)
+
+
+def test_sp_layernorm_padded_strides():
+    # partials and outputs with padded (16-byte aligned) row strides keep the register path
+    wid, t, M, d, N = 3950, 3, 32, 1024, 4
+    P, rbits, res, keep, gamma, beta = inputs(wid, t, M, d, 0.1, True)
+    note("sp_layernorm padded strides")
+    pp = torch.zeros((t, M, d + 64), dtype=torch.float32, device=dev())
+    pp[:, :, :d] = f32_tensor(P)
+    yb = torch.zeros((M, d + 32), dtype=torch.bfloat16, device=dev())
+    xb = torch.zeros((M, d + 16), dtype=torch.float32, device=dev())
+    tp.sp_layernorm(pp[:, :, :d], f32_tensor(gamma), f32_tensor(beta), N, residual=bf16_tensor(rbits),
+                    keep=torch.from_numpy(keep).to(dev()), p_drop=0.1, eps=EPS, out=yb[:, :d], residual_out=xb[:, :d])
+    rx, ry = oracle.sp_layernorm(list(P), res, keep, 0.1, gamma, beta, EPS, N)
+    assert_close(host(yb[:, :d]), ry, "padded y", stored_bf16=True)
+    assert_close(host(xb[:, :d]), rx, "padded x")
+    # the padding columns are untouched
+    assert torch.count_nonzero(yb[:, d:]).item() == 0 and torch.count_nonzero(xb[:, d:]).item() == 0
+
+
+def test_token_all_gather_converts_bf16_to_f32():
+    n, R, C = 3, 5, 64
+    bits, vals = normal_bf16((n, R, C), 1.0, 3960, 0)
+    note("reduce_partials axis=tokens bf16 -> fp32")
+    got = host(tp.reduce_partials(bf16_tensor(bits), axis="tokens", out_dtype=torch.float32))
+    assert_exact(got, oracle.all_gather_rows(list(vals)), "token all-gather bf16 -> fp32")
