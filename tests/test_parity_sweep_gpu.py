@@ -1,0 +1,77 @@
+"""GPU parity over a seeded sweep of shapes, against the float64 oracle.
+
+Each case draws its own sizes from a fixed seed: the token count M crosses the
+skinny (M <= 32), large-tile and partial-tile paths; K, the shard width and the
+shard count N take values that leave ragged k tails and partial column tiles;
+a few cases use sizes that are not multiples of 8 and so take the element-wise
+path. Column-parallel, row-parallel (partials, then the ascending-order sum)
+and the MLP pair are each checked element by element within the bars of
+tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_sharded_linear_amd as tp
+from synthetic import normal_bf16
+from parity import assert_close, bf16_tensor, host, note
+
+pytestmark = pytest.mark.gpu
+
+CASES = 12
+
+
+def draw(case: int, kind: int):
+    """Sizes of one case: (M, K, width, N, s0, ns, act, out_dtype, aligned)."""
+    rng = np.random.default_rng([7000 + kind, case])
+    aligned = case % 4 != 3
+    M = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 700))]))
+    N = int(rng.integers(1, 5))
+    step = 8 if aligned else 1
+    K = step * int(rng.integers(1, 1100 // step + 1))
+    width = step * int(rng.integers(1, 400 // step + 1))
+    s0 = int(rng.integers(0, N))
+    ns = int(rng.integers(1, N - s0 + 1))
+    act = "gelu" if rng.random() < 0.5 else "none"
+    out_dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    return M, K, width, N, s0, ns, act, out_dtype, aligned
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_sweep_col(case):
+    M, K, width, N, s0, ns, act, out_dtype, aligned = draw(case, 0)
+    xb, x = normal_bf16((M, K), 1.0, 7100 + case, 0)
+    wb, w = normal_bf16((K, width * N), 0.02, 7100 + case, 1)
+    note(f"sweep col case={case} M={M} K={K} width={width} N={N} s0={s0} ns={ns} act={act} out={out_dtype}")
+    got = host(tp.col_linear(bf16_tensor(xb), bf16_tensor(wb), N, s0=s0, ns=ns, act=act, out_dtype=out_dtype))
+    ref = np.concatenate(oracle.col_shard_outputs(x, w, N, act, s0=s0, ns=ns), axis=1)
+    assert_close(got, ref, f"col case {case}", stored_bf16=out_dtype == torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_sweep_row(case):
+    M, Kb, width, N, s0, ns, _, _, aligned = draw(case, 1)
+    K = Kb * N  # the split dimension must divide evenly
+    nout = width
+    xb, x = normal_bf16((M, K), 1.0, 7200 + case, 0)
+    wb, w = normal_bf16((K, nout), 0.02, 7200 + case, 1)
+    note(f"sweep row case={case} M={M} K={K} Nout={nout} N={N} s0={s0} ns={ns}")
+    P = tp.row_linear(bf16_tensor(xb), bf16_tensor(wb), N, s0=s0, ns=ns)
+    ph = host(P)
+    refs = oracle.row_partials(x, w, N)[s0:s0 + ns]
+    for j, p in enumerate(refs):
+        assert_close(ph[j], p, f"row case {case} partial {s0 + j}")
+    assert_close(host(tp.reduce_partials(P)), oracle.reduce_sum(refs), f"row case {case} sum")
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_sweep_mlp(case):
+    M, d, fw, N, s0, ns, act, _, aligned = draw(case, 2)
+    F = fw * N
+    xb, x = normal_bf16((M, d), 1.0, 7300 + case, 0)
+    w1b, w1 = normal_bf16((d, F), 0.02, 7300 + case, 1)
+    w2b, w2 = normal_bf16((F, d), 0.02, 7300 + case, 2)
+    note(f"sweep mlp case={case} M={M} d={d} F={F} N={N} s0={s0} ns={ns} act={act}")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), N, s0=s0, ns=ns, act=act))
+    assert_close(got, oracle.mlp(x, w1, w2, N, act, s0, ns), f"mlp case {case}")
