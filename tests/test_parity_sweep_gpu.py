@@ -4,9 +4,9 @@ Each case draws its own sizes from a fixed seed: the token count M crosses the
 skinny (M <= 32), large-tile and partial-tile paths; K, the shard width and the
 shard count N take values that leave ragged k tails and partial column tiles;
 a few cases use sizes that are not multiples of 8 and so take the element-wise
-path. Column-parallel, row-parallel (partials, then the ascending-order sum)
-and the MLP pair are each checked element by element within the bars of
-tests/parity.py.
+path. Column-parallel, row-parallel (partials, then the ascending-order sum),
+the MLP pair and the backward pass of each are checked element by element
+within the bars of tests/parity.py.
 """
 import numpy as np
 import pytest
@@ -75,3 +75,54 @@ def test_sweep_mlp(case):
     note(f"sweep mlp case={case} M={M} d={d} F={F} N={N} s0={s0} ns={ns} act={act}")
     got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), N, s0=s0, ns=ns, act=act))
     assert_close(got, oracle.mlp(x, w1, w2, N, act, s0, ns), f"mlp case {case}")
+
+
+# ----------------------------------------------------------------------------- backward passes
+
+BACKWARD_CASES = 8
+
+
+@pytest.mark.parametrize("case", range(BACKWARD_CASES))
+def test_sweep_col_backward(case):
+    M, K, width, N, s0, ns, _, _, _ = draw(case, 3)
+    xb, x = normal_bf16((M, K), 1.0, 7400 + case, 0)
+    wb, w = normal_bf16((K, width * N), 0.02, 7400 + case, 1)
+    yb, dy = normal_bf16((M, width * ns), 1.0, 7400 + case, 2)
+    note(f"sweep col backward case={case} M={M} K={K} width={width} N={N} s0={s0} ns={ns}")
+    P, G = tp.col_linear_backward(bf16_tensor(xb), bf16_tensor(wb), bf16_tensor(yb), N, s0, ns)
+    partials, dws = oracle.col_linear_backward(x, w, dy, N, s0, ns)
+    ph = host(P)
+    for j in range(ns):
+        assert_close(ph[j], partials[j], f"col backward case {case} dX partial {j}")
+    assert_close(host(G), oracle.concat_cols(dws), f"col backward case {case} dW")
+
+
+@pytest.mark.parametrize("case", range(BACKWARD_CASES))
+def test_sweep_row_backward(case):
+    M, Kb, nout, N, s0, ns, _, _, _ = draw(case, 4)
+    K = Kb * N
+    xb, x = normal_bf16((M, K), 1.0, 7500 + case, 0)
+    wb, w = normal_bf16((K, nout), 0.02, 7500 + case, 1)
+    yb, dy = normal_bf16((M, nout), 1.0, 7500 + case, 2)
+    note(f"sweep row backward case={case} M={M} K={K} Nout={nout} N={N} s0={s0} ns={ns}")
+    A, G = tp.row_linear_backward(bf16_tensor(xb), bf16_tensor(wb), bf16_tensor(yb), N, s0, ns)
+    dxs, dws = oracle.row_linear_backward(x, w, dy, N, s0, ns)
+    assert_close(host(A), oracle.concat_cols(dxs), f"row backward case {case} dX")
+    assert_close(host(G), np.vstack(dws), f"row backward case {case} dW")
+
+
+@pytest.mark.parametrize("case", range(BACKWARD_CASES))
+def test_sweep_mlp_backward(case):
+    M, d, fw, N, s0, ns, act, _, _ = draw(case, 5)
+    F = fw * N
+    xb, x = normal_bf16((M, d), 1.0, 7600 + case, 0)
+    w1b, w1 = normal_bf16((d, F), 0.02, 7600 + case, 1)
+    w2b, w2 = normal_bf16((F, d), 0.02, 7600 + case, 2)
+    yb, dy = normal_bf16((M, d), 1.0, 7600 + case, 3)
+    note(f"sweep mlp backward case={case} M={M} d={d} F={F} N={N} s0={s0} ns={ns} act={act}")
+    dX, dW1, dW2 = tp.mlp_backward(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), bf16_tensor(yb), N,
+                                   s0=s0, ns=ns, act=act)
+    rx, r1, r2 = oracle.mlp_backward(x, w1, w2, dy, N, act, s0, ns)
+    assert_close(host(dX), rx, f"mlp backward case {case} dX")
+    assert_close(host(dW1), r1, f"mlp backward case {case} dW1")
+    assert_close(host(dW2), r2, f"mlp backward case {case} dW2")
