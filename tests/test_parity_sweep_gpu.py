@@ -6,7 +6,10 @@ shard count N take values that leave ragged k tails and partial column tiles;
 a few cases use sizes that are not multiples of 8 and so take the element-wise
 path. Column-parallel, row-parallel (partials, then the ascending-order sum),
 the MLP pair and the backward pass of each are checked element by element
-within the bars of tests/parity.py.
+within the bars of tests/parity.py, and so are attention (head counts,
+grouped key/value heads, head sizes, sequence lengths and counts, causal or
+not, shard subsets) and the sequence-parallel LayerNorm (token and shard
+counts, widths, partial counts, dropout rates, dtypes).
 """
 import numpy as np
 import pytest
@@ -126,3 +129,59 @@ def test_sweep_mlp_backward(case):
     assert_close(host(dX), rx, f"mlp backward case {case} dX")
     assert_close(host(dW1), r1, f"mlp backward case {case} dW1")
     assert_close(host(dW2), r2, f"mlp backward case {case} dW2")
+
+
+# ----------------------------------------------------------------------------- attention and sequence parallelism
+
+ATTN_CASES = 10
+
+
+def draw_attention(case: int):
+    """(heads, kv_heads, head_dim, n, s0, ns, seq_len, sequences, causal) of one attention case."""
+    rng = np.random.default_rng([7700, case])
+    n = int(rng.choice([1, 2, 4]))
+    heads = n * int(rng.integers(1, 4))
+    # key/value heads: a divisor of heads that is either split evenly or replicated (one per shard)
+    options = [k for k in range(1, heads + 1) if heads % k == 0 and (k % n == 0 or (k < n and n % k == 0))]
+    kv_heads = int(rng.choice(options))
+    dh = int(rng.choice([64, 128]))
+    s0 = int(rng.integers(0, n))
+    ns = int(rng.integers(1, n - s0 + 1))
+    seq_len = int(rng.integers(1, 600))
+    sequences = int(rng.integers(1, 4))
+    causal = bool(rng.random() < 0.7)
+    return heads, kv_heads, dh, n, s0, ns, seq_len, sequences, causal
+
+
+@pytest.mark.parametrize("case", range(ATTN_CASES))
+def test_sweep_attention(case):
+    from test_parity_attention_gpu import p_rounding_allowance, qkv_case
+
+    heads, kv_heads, dh, n, s0, ns, L, B, causal = draw_attention(case)
+    bits, q = qkv_case(B * L, heads, kv_heads, dh, n, ns, 7800 + case)
+    note(f"sweep attention case={case} heads={heads} kv_heads={kv_heads} dh={dh} n={n} s0={s0} ns={ns} "
+         f"L={L} B={B} causal={causal}")
+    got = host(tp.attention(bf16_tensor(bits), n, heads, kv_heads, dh, L, causal, s0=s0, ns=ns))
+    ref = oracle.attention(q, n, heads, kv_heads, dh, L, causal, s0, ns)
+    assert_close(got, ref, f"attention case {case}", stored_bf16=True,
+                 extra=p_rounding_allowance(q, n, heads, kv_heads, dh, L, causal, s0, ns))
+
+
+SP_CASES = 8
+
+
+@pytest.mark.parametrize("case", range(SP_CASES))
+def test_sweep_sp_layernorm(case):
+    from test_parity_sp_gpu import run_case
+
+    rng = np.random.default_rng([7900, case])
+    N = int(rng.choice([1, 2, 4, 8]))
+    M = N * int(rng.integers(1, 40))
+    d = int(rng.choice([int(rng.integers(1, 300)), 4 * int(rng.integers(1, 1500))]))
+    t = int(rng.integers(1, 9))
+    s0 = int(rng.integers(0, N))
+    ns = int(rng.integers(1, N - s0 + 1))
+    p_drop = float(rng.choice([0.0, 0.1, 0.5]))
+    r_bf16 = bool(rng.random() < 0.5)
+    y_dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    run_case(8000 + case, t, M, d, N, s0, ns, p_drop=p_drop, r_bf16=r_bf16, y_dtype=y_dtype)
