@@ -22,7 +22,9 @@
 //   O^T += V^T P^T: the probabilities go straight from the S^T accumulators
 //     into the B operand. The contraction order over a block's keys is free,
 //     so it is chosen to match where the accumulators hold them, and the V^T
-//     operand is read with ds_read_b64_tr_b16 in that same key order.
+//     operand is read with ds_read_b64_tr_b16 in that same key order. The
+//     softmax normalizer sums the probabilities as rounded to bf16 for this
+//     product, so the weights that reach V add up to one.
 // K and V tiles come into LDS with LDS-mode buffer loads, two stages deep,
 // shared by the 4 waves. Key blocks that every query of the workgroup sees
 // run first, with no mask and no branch around their loads; the blocks on the
@@ -38,6 +40,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -231,16 +234,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
         for (int t = 0; t < DT; ++t) o[t] *= alpha;
       }
       const float mc = m_run * c;
-      float lsum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, -mc));
-          s[kt][e] = pv;
-          lsum += pv;
-        }
-      l_run += lsum;
+        for (int e = 0; e < 16; ++e) s[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, -mc));
+      float lsum = 0.f;
       // O^T += V^T P^T, 16 keys per step; step t takes elements 8 (t % 2) .. + 7 of tile t / 2,
       // i.e. keys 16 t + 8 (i / 4) + 4 hh + i % 4 for i = 0..7 (the k order of this step).
 #pragma unroll
@@ -248,6 +246,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
         bf16x8 pf;
 #pragma unroll
         for (int i = 0; i < 8; ++i) pf[i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
+        // the normalizer sums the probabilities as rounded for the product, two per dot instruction
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, lsum, false);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           bf16x4 half[2];
@@ -263,6 +267,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[dt], 0, 0, 0);
         }
       }
+      l_run += lsum;
     };
 
     // blocks whose keys every query of the workgroup sees, and are inside the sequence

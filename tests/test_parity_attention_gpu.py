@@ -26,10 +26,11 @@ pytestmark = pytest.mark.gpu
 def p_rounding_allowance(qkv, n, heads, kv_heads, dh, seq_len, causal=True, s0=0, ns=None):
     """Bound on the error from rounding the probabilities to bf16 before the product with V.
 
-    Each probability p_j carries a relative rounding error of at most 2^-9 while the
-    normalizer keeps the unrounded fp32 sum, so |dO_i| <= 2^-9 * sum_j (p_j / l) |v_j|:
-    the attention output with every value replaced by its magnitude, times 2^-9. Twice that
-    is allowed (the fp32 exponentials and sums add their own, smaller, error).
+    Each probability p_j carries a relative rounding error of at most 2^-9 and the
+    normalizer is the sum of the rounded values, so each weight p_j / l moves by at most
+    2^-8 of itself and |dO_i| <= 2^-8 * sum_j (p_j / l) |v_j|: the attention output with
+    every value replaced by its magnitude, times 2^-8. That much is allowed (the fp32
+    exponentials and sums add their own, smaller, error).
     """
     ns = n - s0 if ns is None else ns
     hq = heads // n
