@@ -266,7 +266,8 @@ tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matr
  *   A    logical [M, ns*hq*head_dim], dtype of QKV; shard j's block holds its
  *        query heads' outputs in order: the X of the row-parallel W_o.
  *   M must be a multiple of seq_len. bf16 with head_dim 64 or 128 runs on the
- *   matrix cores (fp32 scores and softmax, probabilities rounded to bf16);
+ *   matrix cores (fp32 scores and softmax, probabilities rounded to bf16 for
+ *   the product with V and normalized by the fp32 sum of those rounded values);
  *   other cases take an fp32 element-wise kernel limited to seq_len <= 8192
  *   (TP_ERR_TOO_LARGE beyond).
  */
