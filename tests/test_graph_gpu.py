@@ -92,3 +92,43 @@ def test_decode_and_attention_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(got_y, y), f"replay {r}: decode MLP differs from eager"
         assert torch.equal(got_a, att), f"replay {r}: attention differs from eager"
+
+
+def test_backward_and_sequence_parallel_boundary_in_a_graph():
+    M, d, F, N = 256, 512, 1024, 4
+    x, w1, w2, dy = inputs(9600, [(M, d), (d, F), (F, d), (M, d)], [1.0, 0.02, 0.02, 1.0])
+    dX = torch.empty((M, d), dtype=torch.float32, device=dev())
+    dW1 = torch.empty((d, F), dtype=torch.float32, device=dev())
+    dW2 = torch.empty((F, d), dtype=torch.float32, device=dev())
+    ws = torch.empty(tp.mlp_backward_workspace_bytes(x, w1, w2, dy, N), dtype=torch.uint8, device=dev())
+    # the sequence-parallel boundary on the row-parallel partials of the forward pass
+    p = torch.empty((N, M, d), dtype=torch.float32, device=dev())
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=dev())
+    gamma = torch.ones(d, dtype=torch.float32, device=dev())
+    beta = torch.zeros(d, dtype=torch.float32, device=dev())
+    ln = torch.empty((M, d), dtype=torch.bfloat16, device=dev())
+
+    def step():
+        tp.mlp_backward(x, w1, w2, dy, N, dx=dX, dw1=dW1, dw2=dW2, workspace=ws)
+        tp.col_linear(x, w1, N, act="gelu", out=h)
+        tp.row_linear(h, w2, N, out=p)
+        tp.sp_layernorm(p, gamma, beta, N, residual=x, out=ln)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(REPLAYS):
+        note(f"graph replay {r}")
+        xs, ys = inputs(9700 + r, [(M, d), (M, d)], [1.0, 1.0])
+        x.copy_(xs)
+        dy.copy_(ys)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (dX, dW1, dW2, ln)]
+        step()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dX", "dW1", "dW2", "LayerNorm"), got, (dX, dW1, dW2, ln)):
+            assert torch.equal(a, b), f"replay {r}: {name} differs from eager"
