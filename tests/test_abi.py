@@ -322,3 +322,29 @@ def test_sp_layernorm_validation(lib):
     # nothing to do: zero tokens
     assert ln(m(FAKE, dtype=F32, rows=0, cols=16, stride=128), 2, None, None, 0.0, None, None, 1e-5, 4, 1, 2,
               None, m(FAKE + (1 << 20), dtype=BF16, rows=0, cols=16)) == 0
+
+
+def test_size_limits(lib):
+    """Sizes past the kernels' 32-bit tile, grid and row limits return TP_ERR_TOO_LARGE."""
+    big = (1 << 31)  # one past the largest row or column count a matrix may have
+    r = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    # column-parallel product with 2^31 token rows (the stride keeps the address range plausible)
+    X = m(FAKE, rows=big, cols=8)
+    W = m(FAKE + (1 << 40), rows=8, cols=16)
+    Y = m(FAKE + (2 << 40), rows=big, cols=16)
+    assert col(lib, X, W, 2, 0, 2, 0, Y) == 10
+    assert col(lib, m(FAKE, rows=big - 1, cols=8), W, 2, 0, 2, 0, m(FAKE + 64, rows=big - 1, cols=16)) == 7
+    # sequence-parallel LayerNorm over 2^24 executed token rows (one workgroup per row)
+    rows = 1 << 24
+    P = m(FAKE, dtype=F32, rows=rows, cols=4)
+    Yl = m(FAKE + (1 << 40), dtype=F32, rows=rows, cols=4)
+    G, B = FAKE + (2 << 40), FAKE + (2 << 40) + 64
+    assert lib.tp_sp_layernorm(r(P), 1, None, None, 0.0, G, B, 1e-5, 1, 0, 1, None, r(Yl), None) == 10
+    # one row fewer passes the size check and stops at the next one (an output over the partials)
+    assert lib.tp_sp_layernorm(r(m(FAKE, dtype=F32, rows=rows - 1, cols=4)), 1, None, None, 0.0, G, B, 1e-5, 1,
+                               0, 1, None, r(m(FAKE + 64, dtype=F32, rows=rows - 1, cols=4)), None) == 7
+    # attention without a matrix-core path (fp32) over a sequence longer than the element-wise kernel holds
+    L = 8193
+    Q = m(FAKE, dtype=F32, rows=L, cols=3 * 16)
+    A = m(FAKE + (1 << 40), dtype=F32, rows=L, cols=16)
+    assert lib.tp_attention(r(Q), 1, 0, 1, 1, 1, 16, L, 1, r(A), None) == 10
