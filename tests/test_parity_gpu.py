@@ -187,6 +187,31 @@ def test_generic_path_unaligned_strides():
     assert_exact(host(tp.reduce_partials(P)), oracle.row_linear(xi, wi, 4), "generic row exact")
 
 
+def test_row_strides_past_31_bits_take_the_guarded_path():
+    """Row strides whose 256-row tile span reaches 2^31 bytes leave the large-tile kernel (its
+    buffer offsets are 31-bit) for the element-guarded one, which addresses in 64 bits."""
+    M, K, width, N = 300, 64, 64, 2
+    xb, x = normal_bf16((M, K), 1.0, 510, 0)
+    wb, w = normal_bf16((K, width * N), 0.02, 510, 1)
+    ldx = 1 << 22  # bf16: 256 rows span 2^31 bytes
+    big_x = torch.empty((M, ldx), dtype=torch.bfloat16, device=dev())
+    X = big_x[:, :K]
+    X.copy_(bf16_tensor(xb))
+    W = bf16_tensor(wb)
+    note("guarded path: col with a 2^22-element row stride on X")
+    got = host(tp.col_linear(X, W, N, act="gelu"))
+    assert_close(got, oracle.col_linear(x, w, N, "gelu"), "col, huge X stride", stored_bf16=True)
+    ldy = 1 << 21  # fp32: 256 rows span 2^31 bytes
+    big_y = torch.empty((M, ldy), dtype=torch.float32, device=dev())
+    Y = big_y[:, : width * N]
+    note("guarded path: col with a 2^21-element row stride on an fp32 Y")
+    tp.col_linear(bf16_tensor(xb), W, N, out=Y)
+    assert_close(host(Y), oracle.col_linear(x, w, N), "col, huge Y stride")
+    note("guarded path: row partials with a 2^22-element row stride on X")
+    assert_close(host(tp.reduce_partials(tp.row_linear(X, W, N))), oracle.row_linear(x, w, N), "row, huge X stride")
+    del big_x, big_y
+
+
 # ----------------------------------------------------------------------------- skinny kernel
 
 
