@@ -18,7 +18,7 @@ import torch
 import oracle
 import tensor_sharded_linear_amd as tp
 from synthetic import WORKLOADS, normal_bf16
-from parity import assert_close, bf16_tensor, f32_tensor, host, note
+from parity import assert_close, bf16_tensor, dev, f32_tensor, host, note
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,22 @@ def test_attention_elementwise_path():
     bits, vals = qkv_case(3 * L, heads, 2, 32, n, n, 2301)
     got = host(tp.attention(bf16_tensor(bits), n, heads, 2, 32, L, False))
     assert_close(got, oracle.attention(vals, n, heads, 2, 32, L, False), "bf16 dh=32", stored_bf16=True)
+
+
+def test_attention_row_stride_past_31_bits():
+    """A QKV row stride whose sequence span reaches 2^31 bytes leaves the matrix-core kernel
+    (31-bit buffer offsets within a sequence) for the element-wise one."""
+    heads, n, dh, L = 4, 2, 128, 300
+    bits, vals = qkv_case(L, heads, heads, dh, n, n, 2350)
+    ld = 1 << 22  # bf16: 300 rows span more than 2^31 bytes
+    big = torch.empty((L, ld), dtype=torch.bfloat16, device=dev())
+    q = big[:, : bits.shape[1]]
+    q.copy_(bf16_tensor(bits))
+    note("attention with a 2^22-element QKV row stride (element-wise path)")
+    got = host(tp.attention(q, n, heads, heads, dh, L))
+    # the element-wise kernel keeps the probabilities in fp32: only the bf16 storage allowance applies
+    assert_close(got, oracle.attention(vals, n, heads, heads, dh, L), "attention, huge stride", stored_bf16=True)
+    del big
 
 
 def test_attention_determinism():
