@@ -269,7 +269,8 @@ tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matr
  *   matrix cores (fp32 scores and softmax, probabilities rounded to bf16 for
  *   the product with V and normalized by the fp32 sum of those rounded values);
  *   other cases take an fp32 element-wise kernel limited to seq_len <= 8192
- *   (TP_ERR_TOO_LARGE beyond).
+ *   (TP_ERR_TOO_LARGE beyond). At most 65535 executed query heads (ns*hq) and
+ *   65535 sequences per call (TP_ERR_TOO_LARGE beyond).
  */
 tp_status tp_attention(const tp_matrix* QKV, int32_t N, int32_t s0, int32_t ns, int32_t heads, int32_t kv_heads,
                        int32_t head_dim, int64_t seq_len, int32_t causal, const tp_matrix* A, void* stream);

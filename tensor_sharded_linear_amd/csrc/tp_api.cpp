@@ -818,6 +818,8 @@ tp_status tp_attention(const tp_matrix* QKV, int32_t N, int32_t s0, int32_t ns, 
   const int64_t blk = (int64_t)(hq + 2 * hkv) * head_dim, oblk = (int64_t)hq * head_dim;
   if (QKV->cols != (int64_t)ns * blk || A->rows != M || A->cols != (int64_t)ns * oblk) return TP_ERR_SHAPE;
   if (M % seq_len != 0) return TP_ERR_SHAPE;
+  // the launch grid has one row per executed head and one layer per sequence
+  if ((int64_t)hq * ns > 65535 || M / seq_len > 65535) return TP_ERR_TOO_LARGE;
   tp_status st;
   if ((st = check_matrix(QKV, ns, M, blk, QKV->cols)) != TP_OK) return st;
   if ((st = check_matrix(A, ns, M, oblk, A->cols)) != TP_OK) return st;

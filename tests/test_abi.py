@@ -348,3 +348,10 @@ def test_size_limits(lib):
     Q = m(FAKE, dtype=F32, rows=L, cols=3 * 16)
     A = m(FAKE + (1 << 40), dtype=F32, rows=L, cols=16)
     assert lib.tp_attention(r(Q), 1, 0, 1, 1, 1, 16, L, 1, r(A), None) == 10
+    # more executed heads, or more sequences, than the launch grid holds
+    Qh = m(FAKE, dtype=BF16, rows=4, cols=3 * 65536 * 16)
+    Ah = m(FAKE + (1 << 40), dtype=BF16, rows=4, cols=65536 * 16)
+    assert lib.tp_attention(r(Qh), 1, 0, 1, 65536, 65536, 16, 4, 1, r(Ah), None) == 10
+    Qs = m(FAKE, dtype=BF16, rows=65536, cols=3 * 16)
+    As = m(FAKE + (1 << 40), dtype=BF16, rows=65536, cols=16)
+    assert lib.tp_attention(r(Qs), 1, 0, 1, 1, 1, 16, 1, 1, r(As), None) == 10
