@@ -106,10 +106,22 @@ hipError_t launch_typed(const GemmDesc& d, dim3 grid, int tiles_n, hipStream_t s
 hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t stream) {
   const int64_t tiles_m = (d.M + TM - 1) / TM, tiles_n = (d.N + TN - 1) / TN;
   if (tiles_m * tiles_n <= 0 || d.batch <= 0) return hipSuccess;
-  if (tiles_m * tiles_n > 0x7fffffff || d.batch > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)d.batch);
-  return d.in_bf16 ? launch_typed<__bf16>(d, grid, (int)tiles_n, stream)
-                   : launch_typed<float>(d, grid, (int)tiles_n, stream);
+  if (tiles_m * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
+  // the batch index is the grid's second dimension: more than 65535 entries go in several launches
+  const int64_t in_elt = d.in_bf16 ? 2 : 4, out_elt = d.out_kind == OUT_F32 ? 4 : 2;
+  for (int64_t z0 = 0; z0 < d.batch; z0 += 65535) {
+    GemmDesc c = d;
+    c.batch = (int32_t)(d.batch - z0 < 65535 ? d.batch - z0 : 65535);
+    c.A = static_cast<const char*>(d.A) + z0 * d.sA * in_elt;
+    c.B = static_cast<const char*>(d.B) + z0 * d.sB * in_elt;
+    c.C = static_cast<char*>(d.C) + z0 * d.sC * out_elt;
+    if (d.aux) c.aux = static_cast<char*>(d.aux) + z0 * d.sX * in_elt;
+    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)c.batch);
+    const hipError_t e = d.in_bf16 ? launch_typed<__bf16>(c, grid, (int)tiles_n, stream)
+                                   : launch_typed<float>(c, grid, (int)tiles_n, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tp

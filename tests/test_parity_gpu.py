@@ -212,6 +212,21 @@ def test_row_strides_past_31_bits_take_the_guarded_path():
     del big_x, big_y
 
 
+def test_more_shards_than_one_launch_grid_holds():
+    """65540 row shards of one input feature each: the element-guarded products go out in
+    several launches (65535 shards per grid), then the sum runs over all partials."""
+    M, N, Nout = 2, 65540, 3
+    x = int_uniform_f32((M, N), -2, 2, 520, 0)
+    w = int_uniform_f32((N, Nout), -2, 2, 520, 1)
+    note(f"row split into {N} shards (fp32, exact)")
+    P = tp.row_linear(f32_tensor(x), f32_tensor(w), N)
+    ph = host(P)
+    want = oracle.row_partials(x, w, N)
+    for s in (0, 1, 65534, 65535, 65536, N - 1):  # both sides of the launch boundary
+        assert_exact(ph[s], want[s], f"partial {s}")
+    assert_exact(host(tp.reduce_partials(P)), oracle.row_linear(x, w, N), "sum over 65540 partials")
+
+
 # ----------------------------------------------------------------------------- skinny kernel
 
 
