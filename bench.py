@@ -10,10 +10,12 @@ W2 [16384, 4096], N = 8. The three calls are exactly the ones tp_mlp issues
 for this shape; calling them one by one lets HIP events on the launch stream
 time each kernel inside the timed region.
 
-Prints one JSON line (rank 0). Extra workloads (the attention projections, one
-shard of a GPT-3-width MLP, and the decode-shaped MLP reported in HBM GB/s)
-are measured too and listed under "secondary"; --workload picks one.
-Only one GPU is used: --gpus above 1 exits with a message.
+Prints one JSON line. Further workloads are measured too and listed under
+"secondary": the same step as one tp_mlp call, the attention projections, one
+shard of a GPT-3-width MLP, the decode-shaped MLP (reported in HBM GB/s), the
+MLP backward pass, the attention block (projections with attention between
+them) and the MLP followed by the sequence-parallel LayerNorm boundary;
+--workload picks one. Only one GPU is used: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
 
