@@ -14,7 +14,8 @@ Prints one JSON line. Further workloads are measured too and listed under
 "secondary": the same step as one tp_mlp call, the attention projections, one
 shard of a GPT-3-width MLP, the decode-shaped MLP (reported in HBM GB/s), the
 MLP backward pass, the attention block (projections with attention between
-them) and the MLP followed by the sequence-parallel LayerNorm boundary;
+them), the MLP followed by the sequence-parallel LayerNorm boundary, and the
+explicit all-gather of the QKV column blocks from shard-major buffers (HBM GB/s);
 --workload picks one. Only one GPU is used: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -37,7 +38,9 @@ LEAD_CYCLES = 40_000_000  # ~20 ms of GPU spin at the ~2 GHz shader clock
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # Workloads that reuse the shapes of another one.
 BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp", "attn_block": "attn_proj", "mlp_sp_block": "megatron_mlp",
-                 "megatron_mlp_call": "megatron_mlp"}
+                 "megatron_mlp_call": "megatron_mlp", "qkv_all_gather": "attn_proj"}
+# Workloads reported in HBM GB/s rather than TFLOP/s.
+HBM_WORKLOADS = ("decode_mlp", "qkv_all_gather")
 SP_P_DROP = 0.1
 ATTN_HEADS, ATTN_HEAD_DIM = 64, 128  # the attention-projection workload: d = 8192 = 64 heads x 128
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
@@ -112,6 +115,9 @@ def make_inputs(name, torch, dev):
         t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
         t["wqkv"] = up(normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)[0])
         t["wo"] = up(normal_bf16((wl.d, wl.out), 0.02, wl.wid, 2)[0])
+    elif name == "qkv_all_gather":
+        # the column-parallel QKV outputs of the 8 shards, each in its own buffer (shard-major)
+        t["x"] = up(normal_bf16((wl.N, wl.M, wl.F // wl.N), 1.0, wl.wid, 8)[0])
     elif name == "decode_mlp":
         width = wl.F // wl.N
         t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
@@ -263,6 +269,16 @@ def plan(name, t, torch, tp):
             rec()
 
         return kernels, step
+    if name == "qkv_all_gather":
+        # the explicit all-gather of column blocks: [8][4096, 3072] -> [4096, 24576], bf16
+        y = torch.empty((wl.M, wl.F), dtype=torch.bfloat16, device=dev)
+        kernels = [{"name": "all_gather_cols", "flop": 0.0, "bound": "hbm", "bytes": 2.0 * 2 * wl.M * wl.F}]
+
+        def step(i, rec):
+            tp.reduce_partials(t["x"], "cols", out=y)
+            rec()
+
+        return kernels, step
     if name == "decode_mlp":
         width = wl.F // wl.N
         h = torch.empty((wl.M, wl.F), dtype=torch.bfloat16, device=dev)
@@ -336,7 +352,7 @@ def time_workload(name, steps, warmup, torch, tp):
         entry["frac_hbm_peak"] = entry["alg_gbs"] / PEAK_HBM_GBS
         res["kernels"].append(entry)
     res["tflops"] = total_flop / (res["ms_per_step"] * 1e-3) / 1e12
-    if name == "decode_mlp":
+    if name in HBM_WORKLOADS:
         res["alg_bytes"] = sum(k["bytes"] for k in kernels)
         res["gbs"] = res["alg_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
     res["_kernels_def"] = kernels
@@ -425,7 +441,7 @@ def main():
     ap.add_argument("--workload", default="all",
                     choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp",
                              "megatron_mlp_bwd", "attn_block", "mlp_sp_block",
-                             "megatron_mlp_call"])
+                             "megatron_mlp_call", "qkv_all_gather"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for HBM counter calibration)")
@@ -448,7 +464,7 @@ def main():
     # the one-call form of the headline MLP runs right after it, in the same thermal state
     names = [main_name] if args.workload != "all" else ["megatron_mlp", "megatron_mlp_call", "attn_proj",
                                                         "gpt3_mlp_shard", "decode_mlp", "megatron_mlp_bwd",
-                                                        "attn_block", "mlp_sp_block"]
+                                                        "attn_block", "mlp_sp_block", "qkv_all_gather"]
     results = {}
     for name in names:
         steps = args.steps if name in ("megatron_mlp", "decode_mlp") else max(3, args.steps // 5)
@@ -463,7 +479,7 @@ def main():
 
     wl = WORKLOADS[BASE_WORKLOAD.get(main_name, main_name)]
     metric = METRIC
-    if main_name == "decode_mlp":
+    if main_name in HBM_WORKLOADS:
         unit, value = "GB/s", main["gbs"]
     else:
         unit, value = "TFLOP/s", main["tflops"]
@@ -482,7 +498,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, rounded to bf16)",
         "config": {"workload": main_name, "M": wl.M, "d": wl.d, "F": wl.F, "N": wl.N, "shards_run": wl.ns,
                    "parallelism": f"tp{wl.N} shards executed on 1 GPU"},
-        "frac_of_bf16_peak": (main["tflops"] / PEAK_BF16_TFLOPS) if main_name != "decode_mlp" else None,
+        "frac_of_bf16_peak": (main["tflops"] / PEAK_BF16_TFLOPS) if main_name not in HBM_WORKLOADS else None,
         "roofline": roofline_for(main),
         "ms_per_step_median": main["ms_per_step_median"],
         "sclk_mhz_after": main["sclk_mhz_after"],
@@ -495,8 +511,9 @@ def main():
         r = results[name]
         entry = {"workload": name, "ms_per_step": r["ms_per_step"], "kernels": r["kernels"],
                  "roofline": roofline_for(r)}
-        if name == "decode_mlp":
-            entry.update({"metric": "decode-shape HBM GB/s", "value": r["gbs"], "unit": "GB/s",
+        if name in HBM_WORKLOADS:
+            label = "decode-shape HBM GB/s" if name == "decode_mlp" else "all-gather HBM GB/s"
+            entry.update({"metric": label, "value": r["gbs"], "unit": "GB/s",
                           "frac_of_hbm_peak": r["gbs"] / PEAK_HBM_GBS})
         else:
             entry.update({"metric": "sharded-linear TFLOP/s", "value": r["tflops"], "unit": "TFLOP/s",

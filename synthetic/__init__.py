@@ -16,7 +16,9 @@ Recipe (every workload):
     mask, 6 = LayerNorm gamma, 7 = beta): the residual as a floating input;
     the keep mask as ``random() >= p_drop`` stored as 0/1 bytes (the random
     numbers dropout draws are an input, passed to both sides); gamma and
-    beta as ``mean + sigma * standard_normal(float32)`` in float32.
+    beta as ``mean + sigma * standard_normal(float32)`` in float32;
+  * tensor id 8: the column-parallel outputs of all shards in their own
+    buffers (shard-major), the input of the explicit all-gather.
 Values are dense and unstructured (no sparsity), as in the dense layers the
 tensor-parallelism pages describe.
 """

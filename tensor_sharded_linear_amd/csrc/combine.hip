@@ -89,6 +89,35 @@ __global__ __launch_bounds__(256) void concat_kernel(CombineDesc d) {
   }
 }
 
+// The same gather four elements per lane (8 or 16 bytes each way) for aligned
+// layouts: lanes run along a row of one block, workgroups over column chunks,
+// rows and blocks, so no index needs a division.
+template <bool PBF16, bool YBF16>
+__global__ __launch_bounds__(256) void concat_vec4_kernel(CombineDesc d) {
+  const int64_t c4 = d.cols >> 2;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= c4) return;
+  for (int64_t j = blockIdx.z; j < d.n; j += gridDim.z)
+    for (int64_t r = blockIdx.y; r < d.rows; r += gridDim.y) {
+      const int64_t src = j * d.sP + r * d.ldp + 4 * c;
+      f32x4 v;
+      if (PBF16) {
+        const bf16x4 h = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(static_cast<const __bf16*>(d.P) + src));
+        v[0] = (float)h[0]; v[1] = (float)h[1]; v[2] = (float)h[2]; v[3] = (float)h[3];
+      } else {
+        v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(d.P) + src));
+      }
+      const int64_t dst = d.concat == 2 ? (j * d.rows + r) * d.ldy + 4 * c : r * d.ldy + j * d.cols + 4 * c;
+      if (YBF16) {
+        bf16x4 h;
+        h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(d.Y) + dst) = h;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(d.Y) + dst) = v;
+      }
+    }
+}
+
 dim3 grid_for(int64_t work) {
   int64_t blocks = (work + 255) / 256;
   if (blocks > 8192) blocks = 8192;  // 32 workgroups per CU, grid-stride beyond
@@ -102,6 +131,31 @@ hipError_t launch_combine(const CombineDesc& d, hipStream_t stream) {
   if (d.rows <= 0 || d.cols <= 0 || d.n <= 0) return hipSuccess;
   const dim3 block(256);
   if (d.concat) {
+    const int64_t pe = d.p_bf16 ? 2 : 4, ye = d.y_bf16 ? 2 : 4;
+    const bool vec = (d.cols % 4 == 0) && (d.ldp % 4 == 0) && (d.sP % 4 == 0) && (d.ldy % 4 == 0) &&
+                     (reinterpret_cast<uintptr_t>(d.P) % (4 * pe) == 0) &&
+                     (reinterpret_cast<uintptr_t>(d.Y) % (4 * ye) == 0);
+    if (vec) {
+      // about 32 workgroups per CU in all: rows and blocks beyond the grid are looped over
+      const int64_t cx = (d.cols / 4 + 255) / 256;
+      const int64_t budget = 8192;
+      int64_t gy = (budget + cx - 1) / cx;
+      gy = gy < d.rows ? gy : d.rows;
+      gy = gy < 65535 ? gy : 65535;
+      int64_t gz = budget / (cx * gy);
+      gz = gz < 1 ? 1 : gz;
+      gz = gz < d.n ? gz : d.n;
+      gz = gz < 65535 ? gz : 65535;
+      const dim3 grid((unsigned)cx, (unsigned)gy, (unsigned)gz);
+      if (d.p_bf16) {
+        if (d.y_bf16) concat_vec4_kernel<true, true><<<grid, block, 0, stream>>>(d);
+        else concat_vec4_kernel<true, false><<<grid, block, 0, stream>>>(d);
+      } else {
+        if (d.y_bf16) concat_vec4_kernel<false, true><<<grid, block, 0, stream>>>(d);
+        else concat_vec4_kernel<false, false><<<grid, block, 0, stream>>>(d);
+      }
+      return hipGetLastError();
+    }
     const dim3 grid = grid_for(d.rows * d.cols * d.n);
     if (d.p_bf16) {
       if (d.y_bf16) concat_kernel<true, true><<<grid, block, 0, stream>>>(d);

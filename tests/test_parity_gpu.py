@@ -301,6 +301,17 @@ def test_reduce_and_concat(rows, cols, n):
     assert_close(got16, oracle.reduce_sum(list(p)), "sum bf16 out", stored_bf16=True)
     note(f"concat rows={rows} cols={cols} n={n}")
     assert_exact(host(tp.reduce_partials(P, "cols")), oracle.concat_cols(list(p)), "concat")
+    assert_close(host(tp.reduce_partials(P, "cols", out_dtype=torch.bfloat16)), oracle.concat_cols(list(p)),
+                 "concat fp32 -> bf16", stored_bf16=True)
+    note(f"concat of bf16 blocks rows={rows} cols={cols} n={n}, side by side and stacked by rows")
+    from synthetic import bf16_bits_from_f32, f32_from_bf16_bits
+    bits = bf16_bits_from_f32(p)
+    vals = f32_from_bf16_bits(bits)
+    Pb = bf16_tensor(bits)
+    assert_exact(host(tp.reduce_partials(Pb, "cols", out_dtype=torch.bfloat16)), oracle.concat_cols(list(vals)),
+                 "concat bf16")
+    assert_exact(host(tp.reduce_partials(Pb, "tokens", out_dtype=torch.bfloat16)), oracle.all_gather_rows(list(vals)),
+                 "token gather bf16")
 
 
 # ----------------------------------------------------------------------------- MLP chain
