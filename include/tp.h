@@ -266,9 +266,10 @@ tp_status tp_mlp_backward(const tp_matrix* X, const tp_matrix* W1, const tp_matr
  *   A    logical [M, ns*hq*head_dim], dtype of QKV; shard j's block holds its
  *        query heads' outputs in order: the X of the row-parallel W_o.
  *   M must be a multiple of seq_len. bf16 with head_dim 64 or 128 runs on the
- *   matrix cores (fp32 scores and softmax, probabilities rounded to bf16 for
- *   the product with V and normalized by the fp32 sum of those rounded values);
- *   other cases take an fp32 element-wise kernel limited to seq_len <= 8192
+ *   matrix cores (fp32 scores and softmax; each probability enters the
+ *   product with V as a bf16 pair, its rounded value and rounded remainder,
+ *   which hold it to about 2^-17 of itself; normalized by the fp32 sum of the
+ *   probabilities); other cases take an fp32 element-wise kernel limited to seq_len <= 8192
  *   (TP_ERR_TOO_LARGE beyond). At most 65535 executed query heads (ns*hq) and
  *   65535 sequences per call (TP_ERR_TOO_LARGE beyond).
  */

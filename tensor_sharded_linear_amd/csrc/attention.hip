@@ -22,9 +22,11 @@
 //   O^T += V^T P^T: the probabilities go straight from the S^T accumulators
 //     into the B operand. The contraction order over a block's keys is free,
 //     so it is chosen to match where the accumulators hold them, and the V^T
-//     operand is read with ds_read_b64_tr_b16 in that same key order. The
-//     softmax normalizer sums the probabilities as rounded to bf16 for this
-//     product, so the weights that reach V add up to one.
+//     operand is read with ds_read_b64_tr_b16 in that same key order. Each
+//     probability enters this product as a bf16 pair (rounded value and
+//     rounded remainder, two MFMAs), so P keeps about 16 significant bits
+//     instead of bf16's 8, and the softmax normalizer is the fp32 sum of the
+//     probabilities themselves.
 // K and V tiles come into LDS with LDS-mode buffer loads, two stages deep,
 // shared by the 4 waves. Key blocks that every query of the workgroup sees
 // run first, with no mask and no branch around their loads; the blocks on the
@@ -40,7 +42,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -241,17 +242,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
       float lsum = 0.f;
       // O^T += V^T P^T, 16 keys per step; step t takes elements 8 (t % 2) .. + 7 of tile t / 2,
       // i.e. keys 16 t + 8 (i / 4) + 4 hh + i % 4 for i = 0..7 (the k order of this step).
+      // Each fp32 probability p is carried as two bf16 values, hi = bf16(p) and
+      // lo = bf16(p - hi), and both are multiplied with V: hi + lo holds p to
+      // about 2^-17 of itself, so the weights that reach V are the fp32
+      // probabilities and the normalizer is their fp32 sum.
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        bf16x8 pf;
+        bf16x8 pf, pl;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pf[i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
-        // the normalizer sums the probabilities as rounded for the product, two per dot instruction
-        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, lsum, false);
+        for (int i = 0; i < 8; ++i) {
+          const float pv = s[t >> 1][8 * (t & 1) + i];
+          const __bf16 hi = (__bf16)pv;
+          pf[i] = hi;
+          pl[i] = (__bf16)(pv - (float)hi);
+          lsum += pv;
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           bf16x4 half[2];
@@ -265,6 +270,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
           }
           const bf16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, o[dt], 0, 0, 0);
         }
       }
       l_run += lsum;
