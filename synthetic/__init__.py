@@ -39,6 +39,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "sample_rows",
+    "stratified_rows",
 ]
 
 
@@ -97,6 +98,25 @@ def sample_rows(m: int, count: int = 256, seed: int = 0) -> np.ndarray:
     g = np.random.default_rng([0x5EED, int(seed), int(m)])
     inner = g.choice(np.arange(1, m - 1), size=count - 2, replace=False)
     return np.sort(np.concatenate([[0, m - 1], inner]))
+
+
+def stratified_rows(m: int, seed: int = 0, block: int = 32, tile: int = 256) -> np.ndarray:
+    """A seeded, sorted set of distinct row indices that covers every block of rows.
+
+    It holds the first and the last row of every `tile`-row tile (the last tile
+    may be ragged) and one seeded row inside every `block`-row block, so that
+    every tile of an output and every `block`-row band inside each tile has
+    rows under check. For m = 16384 that is 512 + 128 rows.
+    """
+    if m <= 0:
+        return np.arange(0)
+    g = np.random.default_rng([0x57A7, int(seed), int(m), int(block), int(tile)])
+    picks = []
+    for t0 in range(0, m, tile):
+        picks += [t0, min(t0 + tile, m) - 1]
+    for b0 in range(0, m, block):
+        picks.append(int(g.integers(b0, min(b0 + block, m))))
+    return np.unique(np.asarray(picks, dtype=np.int64))
 
 
 @dataclass(frozen=True)

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import tensor_sharded_linear_amd as tp
-from synthetic import WORKLOADS, bf16_bits_from_f32, int_uniform_f32, normal_bf16, sample_rows
+from synthetic import WORKLOADS, bf16_bits_from_f32, int_uniform_f32, normal_bf16, stratified_rows
 from parity import assert_close, assert_exact, bf16_tensor, dev, f32_tensor, host, note
 
 pytestmark = pytest.mark.gpu
@@ -217,11 +217,11 @@ def test_mlp_backward_megatron_full_size():
     dX, dW1, dW2 = tp.mlp_backward(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), bf16_tensor(yb), wl.N)
     gx, g1, g2 = host(dX), host(dW1), host(dW2)
     # dX: a row depends only on the same rows of X and dY
-    rows = sample_rows(wl.M, 256, 11)
+    rows = stratified_rows(wl.M, 11)
     rx, _, _ = oracle.mlp_backward(x[rows], w1, w2, dy[rows], wl.N)
     assert_close(gx[rows], rx, "dX sampled rows")
     # dW2 rows f and dW1 columns f depend on column f of Z = X W1 and row f of W2
-    fs = sample_rows(wl.F, 256, 12)
+    fs = stratified_rows(wl.F, 12)
     z = oracle.matmul(x, w1[:, fs])
     h = oracle.gelu(z)
     dz = oracle.matmul(dy, oracle.transpose(w2[fs, :])) * oracle.gelu_grad(z)

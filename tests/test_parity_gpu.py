@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import tensor_sharded_linear_amd as tp
-from synthetic import WORKLOADS, int_uniform_f32, normal_bf16, sample_rows
+from synthetic import WORKLOADS, int_uniform_f32, normal_bf16, stratified_rows
 from parity import assert_close, assert_exact, bf16_tensor, dev, f32_tensor, host, note
 
 pytestmark = pytest.mark.gpu
@@ -394,7 +394,9 @@ def test_determinism_bitwise():
 
 
 def _rows(m):
-    return sample_rows(m, 256, seed=m)
+    """Rows checked at full size: the first and last row of every 256-row tile and one seeded row in
+    every 32-row band (every output tile and every band of 32 accumulator rows inside it)."""
+    return stratified_rows(m, seed=m)
 
 
 def test_megatron_mlp_full_size():
@@ -416,9 +418,17 @@ def test_attention_projections_full_size():
     ab, a = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 3)
     rows = _rows(wl.M)
     note("attention QKV column-parallel full size: X [4096,8192] Wqkv [8192,24576] N=8 -> bf16")
-    qkv = host(tp.col_linear(bf16_tensor(xb), bf16_tensor(wqb), wl.N))
-    assert_close(qkv[rows], oracle.col_linear(x[rows], wq, wl.N), "qkv sampled rows", stored_bf16=True)
+    X, Wq = bf16_tensor(xb), bf16_tensor(wqb)
+    qkv = host(tp.col_linear(X, Wq, wl.N))
+    ref = oracle.col_linear(x[rows], wq, wl.N)
+    assert_close(qkv[rows], ref, "qkv sampled rows", stored_bf16=True)
     del qkv
+    # the same product with fp32 output: the computed value itself, under the plain bar
+    note("attention QKV column-parallel full size with fp32 output")
+    qkv32 = tp.col_linear(X, Wq, wl.N, out_dtype=torch.float32)
+    got32 = host(qkv32[torch.as_tensor(rows, device=qkv32.device)])
+    del qkv32
+    assert_close(got32, ref, "qkv fp32 sampled rows")
     note("attention output projection row-parallel full size: A [4096,8192] Wo [8192,8192] N=8")
     P = tp.row_linear(bf16_tensor(ab), bf16_tensor(wob), wl.N)
     Y = host(tp.reduce_partials(P))

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import tensor_sharded_linear_amd as tp
-from synthetic import WORKLOADS, keep_mask, normal_bf16, normal_f32, sample_rows
+from synthetic import WORKLOADS, keep_mask, normal_bf16, normal_f32, stratified_rows
 from parity import assert_close, assert_exact, bf16_tensor, dev, f32_tensor, host, note
 
 pytestmark = pytest.mark.gpu
@@ -176,7 +176,7 @@ def test_megatron_mlp_then_sp_layernorm_full_size():
                             out_dtype=torch.bfloat16, residual_out=True, partitioned=True)
     yh = host(y).reshape(wl.M, wl.d)
     xh = host(x1).reshape(wl.M, wl.d)
-    rows = sample_rows(wl.M, 256, seed=wl.M + 1)
+    rows = stratified_rows(wl.M, seed=wl.M + 1)
     parts = oracle.mlp_shard_partials(x[rows], w1, w2, wl.N, "gelu")
     rx, ry = oracle.sp_layernorm(parts, x[rows], keep[rows], 0.1, gamma, beta, EPS, 1)
     assert_close(xh[rows], rx, "pre-norm sum, sampled rows")
