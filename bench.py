@@ -2,21 +2,24 @@
 """Benchmark of the tensor-parallel sharded linear layer on one MI355X.
 
 One step is one pass of the whole sharded MLP hot path over one batch of
-seeded synthetic input already resident in HBM: the column-parallel product
-with the GeLU epilogue (the intermediate stays partitioned by shard), the
-row-parallel products into fp32 partials, and the partial-sum reduce, for all
-N shards of the Megatron MLP block X [2048, 4096], W1 [4096, 16384],
-W2 [16384, 4096], N = 8. The three calls are exactly the ones tp_mlp issues
-for this shape; calling them one by one lets HIP events on the launch stream
-time each kernel inside the timed region.
+seeded synthetic input already resident in HBM. The headline workload is one
+GPU's share of a GPT-3-width MLP, the largest configuration that fits one GPU
+(shard 0 of N = 8: X [16384, 12288], W1_0 [12288, 6144], W2_0 [6144, 12288]):
+the column-parallel product with the GeLU epilogue, then the row-parallel
+product into the shard's fp32 partial (one shard, so there is no sum). The
+calls are exactly the ones tp_mlp issues for this shape; calling them one by
+one lets HIP events on the launch stream time each kernel inside the timed
+region.
 
 Prints one JSON line. Further workloads are measured too and listed under
-"secondary": the same step as one tp_mlp call, the attention projections, one
-shard of a GPT-3-width MLP, the decode-shaped MLP (reported in HBM GB/s), the
-MLP backward pass, the attention block (projections with attention between
-them), the MLP followed by the sequence-parallel LayerNorm boundary, and the
-explicit all-gather of the QKV column blocks from shard-major buffers (HBM GB/s);
---workload picks one. Only one GPU is used: --gpus above 1 exits with a message.
+"secondary": the Megatron MLP block with all 8 shards and the partial-sum
+reduce (also as one tp_mlp call), the attention projections, the
+decode-shaped MLP (reported in HBM GB/s), the MLP backward pass, the
+attention block (projections with attention between them), the MLP followed
+by the sequence-parallel LayerNorm boundary, and the explicit all-gather of
+the QKV column blocks from shard-major buffers (HBM GB/s); --workload picks
+one. Every workload is timed over at least 20 steps. Only one GPU is used:
+--gpus above 1 exits with a message.
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp", "attn_block": "attn_proj", 
 # Workloads reported in HBM GB/s rather than TFLOP/s.
 HBM_WORKLOADS = ("decode_mlp", "qkv_all_gather")
 SP_P_DROP = 0.1
+MIN_STEPS = 20  # timed steps of every workload, whatever --steps asks for
 ATTN_HEADS, ATTN_HEAD_DIM = 64, 128  # the attention-projection workload: d = 8192 = 64 heads x 128
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
 # peak under "roofline"), with the decode-shaped MLP's HBM GB/s beside it.
@@ -389,15 +393,36 @@ def roofline_for(res):
             "ms_per_launch": k["ms"]}
 
 
-def cpu_baseline(seconds_target: float = 12.0):
-    """The float64 oracle timed on the host cores on a bounded sample of the Megatron MLP workload."""
-    import oracle
-    from synthetic import WORKLOADS, normal_bf16
+def host_cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it (read-only), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    wl = WORKLOADS["megatron_mlp"]
+
+def cpu_baseline(seconds_target: float = 12.0, sample_rows_count: int = 1024):
+    """The float64 oracle timed on the host cores on a bounded sample of the headline workload.
+
+    The sample is `sample_rows_count` seeded token rows of the GPT-3-width MLP shard: every
+    output row depends only on its own input row, so the oracle's time per row is the same on
+    the sample as on all 16384 rows, and the rate (TFLOP/s) extrapolates unchanged.
+    """
+    import oracle
+    from synthetic import WORKLOADS, normal_bf16, sample_rows
+
+    wl = WORKLOADS["gpt3_mlp_shard"]
+    width = wl.F // wl.N
+    rows = sample_rows(wl.M, sample_rows_count, seed=4242)
     _, x = normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)
-    _, w1 = normal_bf16((wl.d, wl.F), 0.02, wl.wid, 1)
-    _, w2 = normal_bf16((wl.F, wl.d), 0.02, wl.wid, 2)
+    x = np.ascontiguousarray(x[rows])
+    _, w1 = normal_bf16((1, wl.d, width), 0.02, wl.wid, 1)
+    _, w2 = normal_bf16((1, width, wl.d), 0.02, wl.wid, 2)
+    w1, w2 = w1[0], w2[0]
     try:
         from threadpoolctl import threadpool_info
 
@@ -405,21 +430,26 @@ def cpu_baseline(seconds_target: float = 12.0):
                       default=1)
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = os.cpu_count() or 1
-    # one whole pass over the workload first, then as many more as fit the time target
+    run = lambda: oracle.mlp_shard_partials(x, w1, w2, 1, "gelu")  # noqa: E731
+    # one pass first, then as many more as fit the time target
     t0 = time.perf_counter()
-    oracle.mlp(x, w1, w2, wl.N, "gelu")
+    run()
     first = time.perf_counter() - t0
-    passes = int(max(1, min(30, round(seconds_target / max(first, 1e-3)))))
+    passes = int(max(1, min(50, round(seconds_target / max(first, 1e-3)))))
     t0 = time.perf_counter()
     for _ in range(passes):
-        oracle.mlp(x, w1, w2, wl.N, "gelu")
+        run()
     dt = time.perf_counter() - t0
-    flops = passes * 2 * 2.0 * wl.M * wl.d * wl.F
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{passes} whole passes over the megatron_mlp workload (all {wl.M} token rows, all "
-                      f"{wl.N} shards, X [{wl.M},{wl.d}], W1 [{wl.d},{wl.F}], W2 [{wl.F},{wl.d}]), float64 "
-                      f"numpy oracle, {dt:.1f} s",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+    flops = passes * 2 * 2.0 * len(rows) * wl.d * width
+    rate = flops / dt / 1e12
+    full_step_s = dt / passes * wl.M / len(rows)
+    return {"value": rate, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} passes over {len(rows)} seeded token rows of gpt3_mlp_shard (X rows "
+                      f"[{len(rows)},{wl.d}], W1_0 [{wl.d},{width}], GeLU, W2_0 [{width},{wl.d}]), float64 "
+                      f"numpy oracle, {dt:.1f} s; extrapolated to all {wl.M} rows by M/{len(rows)} "
+                      f"(rows are independent): {full_step_s:.1f} s per step",
+            "extrapolated": True, "seconds": dt, "full_step_s_extrapolated": full_step_s,
+            "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model()}
 
 
 def copy_calibration(torch, gib: float = 1.0):
@@ -460,14 +490,14 @@ def main():
     import tensor_sharded_linear_amd as tp
 
     tp.library()  # fails loudly if the HIP library is missing
-    main_name = "megatron_mlp" if args.workload in ("all", "megatron_mlp") else args.workload
-    # the one-call form of the headline MLP runs right after it, in the same thermal state
-    names = [main_name] if args.workload != "all" else ["megatron_mlp", "megatron_mlp_call", "attn_proj",
-                                                        "gpt3_mlp_shard", "decode_mlp", "megatron_mlp_bwd",
+    main_name = "gpt3_mlp_shard" if args.workload == "all" else args.workload
+    # the one-call form of the Megatron MLP runs right after its three-call form, in the same thermal state
+    names = [main_name] if args.workload != "all" else ["gpt3_mlp_shard", "megatron_mlp", "megatron_mlp_call",
+                                                        "attn_proj", "decode_mlp", "megatron_mlp_bwd",
                                                         "attn_block", "mlp_sp_block", "qkv_all_gather"]
     results = {}
     for name in names:
-        steps = args.steps if name in ("megatron_mlp", "decode_mlp") else max(3, args.steps // 5)
+        steps = max(MIN_STEPS, args.steps)
         print(f"[bench] {name}: warmup {args.warmup}, steps {steps}", file=sys.stderr, flush=True)
         results[name] = time_workload(name, steps, args.warmup, torch, tp)
         results[name]["sclk_mhz_after"] = engine_clock_mhz()
