@@ -18,8 +18,9 @@
  *
  * Conventions shared by every entry point
  *   Memory      Every tp_matrix points to device memory owned by the caller.
- *               The library allocates and frees nothing and keeps no mutable
- *               global state; descriptors are read before the call returns.
+ *               The library allocates and frees nothing; descriptors are read
+ *               before the call returns. Apart from tp_mlp_noalloc's scratch
+ *               array (see there) it keeps no mutable global state.
  *   Streams     Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *               stream) and the call returns without waiting. Inputs must
  *               stay alive and unchanged until the stream has passed the work.
@@ -180,6 +181,27 @@ tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const 
 tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, int32_t N, int32_t s0,
                  int32_t ns, int32_t act, void* workspace, size_t* workspace_bytes, const tp_matrix* Y,
                  void* stream);
+
+/*
+ * tp_mlp without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation). Same arguments, result and kernels as tp_mlp; the
+ * intermediate and the partials live in a scratch array built into the
+ * library, one copy per GPU, tp_mlp_noalloc_max_scratch() bytes (64 MiB),
+ * held from the loading of the library until the process ends. The call
+ * allocates and frees nothing. Shapes whose tp_mlp workspace exceeds that
+ * size return TP_ERR_TOO_LARGE with nothing enqueued. The scratch array's
+ * device address is looked up on the first call made with a device current;
+ * that device must be the one `stream` belongs to. Every call on one GPU
+ * shares that GPU's array and leaves its contents behind: calls that may run
+ * at the same time on one GPU (different streams, or host threads) race
+ * and must be ordered by the caller; calls on one stream are ordered by it.
+ */
+tp_status tp_mlp_noalloc(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, int32_t N, int32_t s0,
+                         int32_t ns, int32_t act, const tp_matrix* Y, void* stream);
+
+/* Bytes of the per-GPU scratch array tp_mlp_noalloc uses. */
+size_t tp_mlp_noalloc_max_scratch(void);
 
 /*
  * Backward passes. The pages pair every forward collective with a backward

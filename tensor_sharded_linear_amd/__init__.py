@@ -26,6 +26,8 @@ __all__ = [
     "reduce_partials",
     "mlp",
     "mlp_workspace_bytes",
+    "mlp_noalloc",
+    "mlp_noalloc_max_scratch",
     "col_linear_backward",
     "row_linear_backward",
     "mlp_backward",
@@ -217,6 +219,30 @@ def mlp(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, n: int, s0: int = 0
                           ctypes.c_void_p(_stream(x)))
     _lib.check(st, "tp_mlp")
     return out
+
+
+def mlp_noalloc(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, n: int, s0: int = 0,
+                ns: int | None = None, act: str = "gelu", out: torch.Tensor | None = None) -> torch.Tensor:
+    """tp_mlp_noalloc: the MLP pair with the library's built-in per-GPU scratch instead of a workspace.
+
+    Raises TpError (TP_ERR_TOO_LARGE) when the shapes need more than mlp_noalloc_max_scratch() bytes.
+    """
+    ns = n - s0 if ns is None else ns
+    _require_gpu(x, w1, w2)
+    xm, w1m, w2m, dout = _mlp_mats(x, w1, w2, n)
+    if out is None:
+        out = torch.empty((x.shape[0], dout), dtype=torch.float32, device=x.device)
+    _require_gpu(out)
+    ym = _full(out)
+    st = library().tp_mlp_noalloc(ctypes.byref(xm), ctypes.byref(w1m), ctypes.byref(w2m), n, s0, ns, _ACTS[act],
+                                  ctypes.byref(ym), ctypes.c_void_p(_stream(x)))
+    _lib.check(st, "tp_mlp_noalloc")
+    return out
+
+
+def mlp_noalloc_max_scratch() -> int:
+    """Bytes of the per-GPU scratch array mlp_noalloc uses."""
+    return int(library().tp_mlp_noalloc_max_scratch())
 
 
 # ----------------------------------------------------------------------------- backward passes

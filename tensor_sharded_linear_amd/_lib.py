@@ -35,6 +35,8 @@ EXPORTS = (
     "tp_row_linear",
     "tp_reduce_partials",
     "tp_mlp",
+    "tp_mlp_noalloc",
+    "tp_mlp_noalloc_max_scratch",
     "tp_col_linear_backward",
     "tp_row_linear_backward",
     "tp_mlp_backward",
@@ -90,6 +92,11 @@ def load() -> ctypes.CDLL:
     lib.tp_mlp.argtypes = [_M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), _M, ctypes.c_void_p]
     lib.tp_mlp.restype = ctypes.c_int32
+    lib.tp_mlp_noalloc.argtypes = [_M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _M,
+                                   ctypes.c_void_p]
+    lib.tp_mlp_noalloc.restype = ctypes.c_int32
+    lib.tp_mlp_noalloc_max_scratch.argtypes = []
+    lib.tp_mlp_noalloc_max_scratch.restype = ctypes.c_size_t
     lib.tp_col_linear_backward.argtypes = [_M, _M, _M, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _M, _M,
                                            ctypes.c_void_p]
     lib.tp_col_linear_backward.restype = ctypes.c_int32

@@ -9,6 +9,7 @@
 // block of the split dimension; the split must be even.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "tp.h"
 #include "tp_internal.h"
@@ -278,6 +279,39 @@ Blocks buffer_blocks(void* ptr, int32_t dtype, int64_t ld, int64_t step) {
 
 }  // namespace
 
+// Scratch memory of tp_mlp_noalloc: a file-scope device array, so that entry
+// point needs no allocation. Every GPU the library runs on holds its own copy
+// (kScratchBytes each) from the loading of the library's code object until the
+// process ends. In host code `scratch` is only a stand-in for the symbol; its
+// device address on each GPU comes from hipGetSymbolAddress and is the only
+// form ever handed to kernels.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+}  // namespace
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxScratchDevices];  // device address of `scratch` per device, resolved once
+
+// The address of the current device's copy of `scratch`, looked up on the
+// first call made with that device current.
+tp_status current_device_scratch(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TP_ERR_HIP;
+  if (dev >= kMaxScratchDevices) return TP_ERR_TOO_LARGE;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TP_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return TP_OK;
+}
+}  // namespace
+
 extern "C" {
 
 tp_status tp_col_linear(const tp_matrix* X, const tp_matrix* W, int32_t N, int32_t s0, int32_t ns, int32_t act,
@@ -534,6 +568,21 @@ tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, i
   }
   return TP_OK;
 }
+
+tp_status tp_mlp_noalloc(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, int32_t N, int32_t s0,
+                         int32_t ns, int32_t act, const tp_matrix* Y, void* stream) {
+  // Shapes, dtypes and strides first (the size query enqueues nothing and needs no pointers).
+  size_t need = 0;
+  tp_status st = tp_mlp(X, W1, W2, N, s0, ns, act, nullptr, &need, Y, stream);
+  if (st != TP_OK) return st;
+  if (need > kScratchBytes) return TP_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if ((st = current_device_scratch(&ws)) != TP_OK) return st;
+  size_t have = kScratchBytes;
+  return tp_mlp(X, W1, W2, N, s0, ns, act, ws, &have, Y, stream);
+}
+
+size_t tp_mlp_noalloc_max_scratch(void) { return kScratchBytes; }
 
 tp_status tp_col_linear_backward(const tp_matrix* X, const tp_matrix* W, const tp_matrix* dY, int32_t N,
                                  int32_t s0, int32_t ns, const tp_matrix* dXp, const tp_matrix* dW,

@@ -355,3 +355,16 @@ def test_size_limits(lib):
     Qs = m(FAKE, dtype=BF16, rows=65536, cols=3 * 16)
     As = m(FAKE + (1 << 40), dtype=BF16, rows=65536, cols=16)
     assert lib.tp_attention(r(Qs), 1, 0, 1, 1, 1, 16, 1, 1, r(As), None) == 10
+
+
+def test_mlp_noalloc_rejects_oversized_shapes_before_any_hip_call(lib):
+    # the Megatron block's workspace (H 67 MB + partials 268 MB) exceeds the built-in scratch
+    assert lib.tp_mlp_noalloc_max_scratch() == 64 << 20
+    X, W1, W2 = m(rows=2048, cols=4096), m(rows=4096, cols=16384), m(rows=16384, cols=4096)
+    Y = m(dtype=F32, rows=2048, cols=4096)
+    st = lib.tp_mlp_noalloc(ctypes.byref(X), ctypes.byref(W1), ctypes.byref(W2), 8, 0, 8, 1, ctypes.byref(Y), None)
+    assert st == 10  # TP_ERR_TOO_LARGE
+    # shape errors are reported as by tp_mlp
+    bad = m(rows=2048, cols=4095)
+    st = lib.tp_mlp_noalloc(ctypes.byref(bad), ctypes.byref(W1), ctypes.byref(W2), 8, 0, 8, 1, ctypes.byref(Y), None)
+    assert st == 3  # TP_ERR_SHAPE
