@@ -14,7 +14,8 @@ region.
 Prints one JSON line. Further workloads are measured too and listed under
 "secondary": the Megatron MLP block with all 8 shards and the partial-sum
 reduce (also as one tp_mlp call), the attention projections, the
-decode-shaped MLP (reported in HBM GB/s), the MLP backward pass, the
+decode-shaped MLP (reported in HBM GB/s, as three timed calls and as one
+tp_mlp call), the MLP backward pass, the
 attention block (projections with attention between them), the MLP followed
 by the sequence-parallel LayerNorm boundary, and the explicit all-gather of
 the QKV column blocks from shard-major buffers (HBM GB/s); --workload picks
@@ -41,9 +42,9 @@ LEAD_CYCLES = 40_000_000  # ~20 ms of GPU spin at the ~2 GHz shader clock
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # Workloads that reuse the shapes of another one.
 BASE_WORKLOAD = {"megatron_mlp_bwd": "megatron_mlp", "attn_block": "attn_proj", "mlp_sp_block": "megatron_mlp",
-                 "megatron_mlp_call": "megatron_mlp", "qkv_all_gather": "attn_proj"}
+                 "megatron_mlp_call": "megatron_mlp", "qkv_all_gather": "attn_proj", "decode_mlp_call": "decode_mlp"}
 # Workloads reported in HBM GB/s rather than TFLOP/s.
-HBM_WORKLOADS = ("decode_mlp", "qkv_all_gather")
+HBM_WORKLOADS = ("decode_mlp", "decode_mlp_call", "qkv_all_gather")
 SP_P_DROP = 0.1
 MIN_STEPS = 20  # timed steps of every workload, whatever --steps asks for
 ATTN_HEADS, ATTN_HEAD_DIM = 64, 128  # the attention-projection workload: d = 8192 = 64 heads x 128
@@ -122,7 +123,7 @@ def make_inputs(name, torch, dev):
     elif name == "qkv_all_gather":
         # the column-parallel QKV outputs of the 8 shards, each in its own buffer (shard-major)
         t["x"] = up(normal_bf16((wl.N, wl.M, wl.F // wl.N), 1.0, wl.wid, 8)[0])
-    elif name == "decode_mlp":
+    elif name in ("decode_mlp", "decode_mlp_call"):
         width = wl.F // wl.N
         t["x"] = up(normal_bf16((wl.M, wl.d), 1.0, wl.wid, 0)[0])
         # two weight sets used alternately, so no step finds the previous step's weights in cache
@@ -283,6 +284,20 @@ def plan(name, t, torch, tp):
             rec()
 
         return kernels, step
+    if name == "decode_mlp_call":
+        # the decode MLP as one tp_mlp call (the same three kernels, launched back to back)
+        y = torch.empty((wl.M, wl.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(tp.mlp_workspace_bytes(t["x"], t["w1s"][0], t["w2s"][0], wl.N), dtype=torch.uint8,
+                         device=dev)
+        kernels = [{"name": "tp_mlp", "flop": 2 * flop(wl.M, wl.d, wl.F), "bound": "hbm",
+                    "bytes": 2.0 * (wl.M * wl.d + 2 * wl.d * wl.F) + 4.0 * wl.M * wl.d}]
+
+        def step(i, rec):
+            r = i % 2
+            tp.mlp(t["x"], t["w1s"][r], t["w2s"][r], wl.N, out=y, workspace=ws)
+            rec()
+
+        return kernels, step
     if name == "decode_mlp":
         width = wl.F // wl.N
         h = torch.empty((wl.M, wl.F), dtype=torch.bfloat16, device=dev)
@@ -297,8 +312,8 @@ def plan(name, t, torch, tp):
         ]
 
         def step(i, rec):
-            # the calls tp_mlp issues for this shape (its K split stays 1 here);
-            # the two weight sets alternate
+            # the three calls tp_mlp issues for this shape (its K split stays 1 here),
+            # with events between them; the two weight sets alternate
             r = i % 2
             tp.col_linear(t["x"], t["w1s"][r], wl.N, act="gelu", out=h)
             rec()
@@ -470,7 +485,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "megatron_mlp", "attn_proj", "gpt3_mlp_shard", "decode_mlp",
-                             "megatron_mlp_bwd", "attn_block", "mlp_sp_block",
+                             "decode_mlp_call", "megatron_mlp_bwd", "attn_block", "mlp_sp_block",
                              "megatron_mlp_call", "qkv_all_gather"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -493,8 +508,9 @@ def main():
     main_name = "gpt3_mlp_shard" if args.workload == "all" else args.workload
     # the one-call form of the Megatron MLP runs right after its three-call form, in the same thermal state
     names = [main_name] if args.workload != "all" else ["gpt3_mlp_shard", "megatron_mlp", "megatron_mlp_call",
-                                                        "attn_proj", "decode_mlp", "megatron_mlp_bwd",
-                                                        "attn_block", "mlp_sp_block", "qkv_all_gather"]
+                                                        "attn_proj", "decode_mlp", "decode_mlp_call",
+                                                        "megatron_mlp_bwd", "attn_block", "mlp_sp_block",
+                                                        "qkv_all_gather"]
     results = {}
     for name in names:
         steps = max(MIN_STEPS, args.steps)
@@ -542,7 +558,7 @@ def main():
         entry = {"workload": name, "ms_per_step": r["ms_per_step"], "kernels": r["kernels"],
                  "roofline": roofline_for(r)}
         if name in HBM_WORKLOADS:
-            label = "decode-shape HBM GB/s" if name == "decode_mlp" else "all-gather HBM GB/s"
+            label = "decode-shape HBM GB/s" if name.startswith("decode_mlp") else "all-gather HBM GB/s"
             entry.update({"metric": label, "value": r["gbs"], "unit": "GB/s",
                           "frac_of_hbm_peak": r["gbs"] / PEAK_HBM_GBS})
         else:
@@ -551,8 +567,9 @@ def main():
         secondary.append(entry)
     if secondary:
         line["secondary"] = secondary
-    if "decode_mlp" in results and main_name != "decode_mlp":
-        line["decode_shape_hbm_gbs"] = results["decode_mlp"]["gbs"]
+    if "decode_mlp_call" in results and main_name != "decode_mlp_call":
+        # the decode MLP as the library offers it: one tp_mlp call
+        line["decode_shape_hbm_gbs"] = results["decode_mlp_call"]["gbs"]
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on host cores)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline()
