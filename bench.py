@@ -51,12 +51,25 @@ ATTN_HEADS, ATTN_HEAD_DIM = 64, 128  # the attention-projection workload: d = 81
 # The headline metric: TFLOP/s of the sharded MLP (its fraction of the bf16
 # peak under "roofline"), with the decode-shaped MLP's HBM GB/s beside it.
 METRIC = "sharded-linear TFLOP/s (% of bf16 MFMA peak); decode-shape HBM GB/s"
-KERNEL_SOURCES = ["gemm_mfma.hip", "gemm_skinny.hip", "combine.hip", "attention.hip", "sp_layernorm.hip"]
+# Kernel sources each workload's kernels are built from: the HBM traffic recorded
+# for a workload is reported only while these files are unchanged.
+WORKLOAD_SOURCES = {
+    "gpt3_mlp_shard": ["gemm_mfma.hip"],
+    "megatron_mlp": ["gemm_mfma.hip", "combine.hip"],
+    "megatron_mlp_call": ["gemm_mfma.hip", "combine.hip"],
+    "attn_proj": ["gemm_mfma.hip", "combine.hip"],
+    "decode_mlp": ["gemm_skinny.hip", "combine.hip"],
+    "decode_mlp_call": ["gemm_skinny.hip", "combine.hip"],
+    "megatron_mlp_bwd": ["gemm_mfma.hip", "combine.hip"],
+    "attn_block": ["gemm_mfma.hip", "attention.hip", "combine.hip"],
+    "mlp_sp_block": ["gemm_mfma.hip", "sp_layernorm.hip"],
+    "qkv_all_gather": ["combine.hip"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in WORKLOAD_SOURCES[workload]:
         with open(os.path.join(ROOT, "tensor_sharded_linear_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -69,9 +82,10 @@ def measured_traffic(workload: str, kernel: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    entry = t.get("workloads", {}).get(workload, {})
+    if entry.get("source_hash") != kernel_source_hash(workload):
         return None
-    return t.get("workloads", {}).get(workload, {}).get(kernel)
+    return entry.get("kernels", {}).get(kernel)
 
 
 # ----------------------------------------------------------------------------- workloads
