@@ -352,6 +352,30 @@ def test_mlp_fp32_exact():
     assert_exact(got, oracle.mlp(x, w1, w2, N, "none"), "fp32 mlp")
 
 
+@pytest.mark.parametrize("M,d,F,N,s0,ns", [(300, 512, 2048, 4, 0, 4), (300, 392, 1536, 3, 0, 3),
+                                           (520, 264, 2048, 8, 2, 5), (64, 512, 1024, 2, 0, 2)])
+def test_mlp_bitwise_equals_separate_calls(M, d, F, N, s0, ns):
+    """tp_mlp must carry the bits of the three public calls it stands for: the column product with
+    GeLU, the row partials of the executed shards, their sum in ascending shard order. The shapes
+    have ragged row and column tiles and shard counts that are not multiples of 4."""
+    xb, _ = normal_bf16((M, d), 1.0, 980 + M, 0)
+    w1b, _ = normal_bf16((d, F), 0.02, 980 + M, 1)
+    w2b, _ = normal_bf16((F, d), 0.02, 980 + M, 2)
+    X, W1, W2 = bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b)
+    width = F // N
+    note(f"mlp vs separate calls M={M} d={d} F={F} N={N} s0={s0} ns={ns}")
+    y = tp.mlp(X, W1, W2, N, s0=s0, ns=ns)
+    h = tp.col_linear(X, W1, N, s0=s0, ns=ns, act="gelu")
+    p = tp.row_linear(h, W2[s0 * width:(s0 + ns) * width], ns)
+    y2 = tp.reduce_partials(p)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    note("mlp vs separate calls, second call on the same shapes")
+    y3 = tp.mlp(X, W1, W2, N, s0=s0, ns=ns)
+    torch.cuda.synchronize()
+    assert torch.equal(y3.view(torch.int32), y2.view(torch.int32))
+
+
 def test_empty_and_degenerate():
     xb, x = normal_bf16((0, 64), 1.0, 960, 0)
     wb, w = normal_bf16((64, 128), 0.02, 960, 1)
