@@ -11,8 +11,11 @@
 // all-reduce): dX = dY W^T takes B transposed, dW = X^T dY takes A transposed.
 //
 // Tile 256 x 256 x 64, 512 threads = 8 waves in a 2 x 4 grid (two waves per
-// SIMD); each wave owns a 128 x 64 block of C held as 4 x 2
-// v_mfma_f32_32x32x16_bf16 accumulators.
+// SIMD); each wave owns a 128 x 64 block of C held as 8 x 4
+// v_mfma_f32_16x16x32_bf16 accumulators. Under the socket's power cap this
+// shape sustains more than the 32 x 32 x 16 one (2.06 against 1.79 PFLOP/s of
+// bare MFMAs on random data, the same cycles per flop on one wave): it moves
+// half the accumulator bytes per flop.
 // Each operand tile goes from HBM straight into LDS with buffer loads in LDS
 // mode (no register staging), two stages deep, in one of two layouts chosen by
 // how the operand is stored:
@@ -21,9 +24,7 @@
 //   MN-rows: 64 k-rows x 256 (of M or N), 512-byte rows (A as [K, M], B as
 //     [K, N], the pages' [in, out] weight); fragments need K-contiguous lanes,
 //     which gfx950 provides with the LDS transpose read ds_read_b64_tr_b16.
-// Up to K = 6144 every wave reads the fragments of the next 16-wide k step
-// while the matrix cores work on the current one (one barrier per k-tile).
-// Beyond, the two waves of each SIMD run a ping-pong schedule: one issues an
+// The two waves of each SIMD run a ping-pong schedule: one issues an
 // uninterrupted cluster of MFMAs while the other reads the next k-tile's
 // fragments and issues loads (see Sched). Rows past M, N or K and k chunks
 // past K read as zero through the buffer range check.
@@ -37,13 +38,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 #define TP_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512;
 constexpr int WM = 128, WN = 64;          // wave tile
-constexpr int FM = WM / 32, FN = WN / 32;  // 32 x 32 fragments per wave
+constexpr int FM = WM / 16, FN = WN / 16;  // 16 x 16 blocks per wave
+constexpr int KS = 32;                     // k per MFMA (v_mfma_f32_16x16x32_bf16)
 constexpr int TILE_BYTES = 256 * BK * 2;   // one LDS stage of one operand: 32 KB
 constexpr int GROUP_M = 4;  // tile rows per group: 32 resident tiles form a 4 x 8 block per XCD
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
@@ -53,6 +55,7 @@ constexpr int kStoreNT = 2;                   // buffer-store cache policy: nont
 struct Params {
   GemmDesc d;
   int tiles_m, tiles_n, total;
+  int vec;  // C (and the side matrix) take 16-byte (fp32) / 8-byte (bf16) stores
 };
 
 // A buffer resource over `bytes` bytes from `base` (both uniform across the wave).
@@ -78,9 +81,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // XOR swizzles of 16-byte chunks that keep the fragment reads free of bank
-// conflicts: K-rows tiles hold 8 chunks per row, MN-rows tiles 32.
+// conflicts: K-rows tiles hold 8 chunks per row, MN-rows tiles 32. In an
+// MN-rows tile the four k-rows one transpose read takes (k-row bits 0-1) and
+// the two 16-lane groups read in the same cycle (k-rows 8 apart, bit 3) land
+// on distinct slots.
 __device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int swz_mn(int krow) { return ((krow & 1) * 6) ^ (((krow >> 1) & 1) * 12); }
+__device__ __forceinline__ int swz_mn(int krow) {
+  return ((krow & 1) * 6) ^ (((krow >> 1) & 1) * 12) ^ (((krow >> 3) & 1) * 2);
+}
 
 // One operand of the product: where its tile comes from and how it is laid out.
 // KROWS: the operand is stored with k contiguous (A [M, K] or B [N, K]).
@@ -128,29 +136,32 @@ struct Operand {
   }
 };
 
-// Fragment reads of F 32-wide blocks starting at row/col `pos` of the tile.
-// Either layout yields the lane format both MFMA operands use: lane l holds
-// row/col (l & 31) of the block and k values 8 (l >> 5) .. + 7 of the k step.
+// Fragment reads of F 16-wide blocks starting at row/col `pos` of the tile,
+// for the 32-deep k step kk of the tile. Either layout yields the lane format
+// both MFMA operands use: lane l holds row/col (l & 15) of the block and k
+// values 8 (l >> 4) .. + 7 of the k step.
 template <bool KROWS, int F>
 struct Frags {
   int off[F];
-  int sw;
   __device__ __forceinline__ void init(int lane, int pos) {
     if (KROWS) {
-      // rows of block f differ from row pos + (lane & 31) by 32 f: swz_k changes by (4 f) & 7
-#pragma unroll
-      for (int f = 0; f < F; ++f) off[f] = (pos + f * 32 + (lane & 31)) * 128;
-      sw = swz_k(pos + (lane & 31));
-    } else {
-      // transpose reads: lane (G = lane >> 4, j = lane & 15) supplies k-row
-      // 8 (G >> 1) + 4 t + (j >> 2) and columns 16 (G & 1) + 4 (j & 3) .. + 3 of a
-      // 32-wide block, and receives 4 k values of column 16 (G & 1) + j
-      const int G = lane >> 4, j16 = lane & 15;
-      const int kr = 8 * (G >> 1) + (j16 >> 2);
-      sw = swz_mn(kr);  // k-rows used with this lane differ by multiples of 4
+      // row pos + 16 f + (l & 15), k chunk 4 kk + (l >> 4); kk only flips bit 2 of the chunk
 #pragma unroll
       for (int f = 0; f < F; ++f) {
-        const int col = pos + f * 32 + 16 * (G & 1) + 4 * (j16 & 3);
+        const int row = pos + f * 16 + (lane & 15);
+        off[f] = row * 128 + (((lane >> 4) ^ swz_k(row)) << 4);
+      }
+    } else {
+      // transpose reads: lane (G = lane >> 4, j = lane & 15) supplies k-row
+      // 32 kk + 8 G + 4 t + (j >> 2) and columns 4 (j & 3) .. + 3 of a 16-wide
+      // block, and receives 4 k values of column j; t and kk leave the k-row
+      // bits the swizzle uses unchanged
+      const int G = lane >> 4, j16 = lane & 15;
+      const int kr = 8 * G + (j16 >> 2);
+      const int sw = swz_mn(kr);
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int col = pos + f * 16 + 4 * (j16 & 3);
         off[f] = kr * 512 + (((col >> 3) ^ sw) << 4) + (col & 4) * 2;
       }
     }
@@ -159,10 +170,9 @@ struct Frags {
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       if (KROWS) {
-        const int kc = kk * 2 + (lane >> 5);
-        out[f] = *reinterpret_cast<const bf16x8*>(stage + off[f] + ((kc ^ sw ^ ((4 * f) & 7)) << 4));
+        out[f] = *reinterpret_cast<const bf16x8*>(stage + (off[f] ^ (kk << 6)));
       } else {
-        const char* p = stage + off[f] + kk * 16 * 512;
+        const char* p = stage + off[f] + kk * KS * 512;
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4 * 512));
         out[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -194,18 +204,24 @@ __device__ __forceinline__ TileCoord tile_coord(const Params& p) {
   return t;
 }
 
-typedef f32x16 AccTile[FM][FN];
+typedef f32x4 AccTile[FM][FN];
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Epilogue: accumulator element e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4,
-// column l % 32 of its 32 x 32 block. Stores go through a buffer resource
+// Epilogue through LDS. Accumulator element e of lane l is row 4 (l / 16) + e,
+// column l % 16 of its 16 x 16 block; stored as it is, every store instruction
+// would write 64-byte pieces of 4 rows. Instead each wave parks 64 of its 128
+// rows in a private 16 KB patch of the (by then idle) LDS stages and reads
+// them back as 4 consecutive columns per lane, so that each store writes 4
+// rows of 64 contiguous columns. The activation, the side matrix and the
+// conversion are applied on the way out. Stores go through a buffer resource
 // over this tile's rows of C: rows past M fall outside it and are dropped;
-// columns past N are masked per lane. The row part of every offset is
-// uniform and travels in the scalar offset. The bf16 side matrix (the saved
-// pre-activation, or the one the GeLU derivative is taken of) has the same
-// shape and is addressed the same way.
+// columns past N are masked per lane (N is a multiple of 8, so a lane's 4
+// columns are all in or all out). `vec`: C (and the side matrix) allow
+// 16-byte (fp32) or 8-byte (bf16) stores; else each value is stored alone.
 template <int OUT, int ACT>
 __device__ __forceinline__ void store_tile(const GemmDesc& d, const AccTile& acc, int64_t m0, int64_t n0, int z,
-                                           int lane, int wm, int wn) {
+                                           int lane, int wm, int wn, float* patch, bool vec) {
   const int64_t N = d.N;
   const int rows_here = (int)min<int64_t>(d.M - m0, BM);
   const int64_t ldc = d.ldc;
@@ -221,52 +237,102 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, const AccTile& acc
     xrsrc = make_rsrc(Xt, ((int64_t)(rows_here - 1) * d.ldx + (N - n0)) * 2);
     xrow_bytes = (uint32_t)(d.ldx * 2);
   }
+  const int g = lane >> 4, j = lane & 15;
+  const int col = wn * WN + 4 * j;  // this lane's 4 columns on the way out
+  const bool in = n0 + col < N;
 #pragma unroll
-  for (int im = 0; im < FM; ++im) {
+  for (int half = 0; half < 2; ++half) {
+    // park rows 64 half .. + 63 of the wave's block: [64][64] fp32, the 16-column
+    // groups of row r XOR-swizzled by (r / 4) % 4 so both directions are conflict-free
 #pragma unroll
-    for (int jn = 0; jn < FN; ++jn) {
-      const int col = wn * WN + jn * 32 + (lane & 31);
-      const int row0 = wm * WM + im * 32 + 4 * (lane >> 5);
-      const bool in = n0 + col < N;
-      const uint32_t voff = in ? (uint32_t)(row0 * row_bytes + col * ES) : kOOB;
-      const uint32_t xoff = in ? (uint32_t)(row0 * xrow_bytes + col * 2) : kOOB;
-      unsigned short zb[16];
-      if (ACT == ACT_DGELU) {
+    for (int rb = 0; rb < FM / 2; ++rb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          zb[e] = __builtin_amdgcn_raw_buffer_load_b16(xrsrc, xoff, (uint32_t)(8 * (e >> 2) + (e & 3)) * xrow_bytes, 0);
+      for (int cb = 0; cb < FN; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = rb * 16 + 4 * g + e;
+          patch[row * 64 + ((cb ^ g) << 4) + j] = acc[half * (FM / 2) + rb][cb][e];
+        }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + g;  // (row / 4) % 4 = i % 4
+      f32x4 v = *reinterpret_cast<const f32x4*>(patch + row * 64 + ((4 * j) ^ (16 * (i & 3))));
+      const int trow = wm * WM + half * 64 + row;  // row within the tile
+      const uint32_t voff = in ? (uint32_t)(trow * row_bytes + col * ES) : kOOB;
+      const uint32_t xoff = in ? (uint32_t)(trow * xrow_bytes + col * 2) : kOOB;
+      if (ACT == ACT_GELU_SAVE) {
+        if (vec) {
+          u32x2 h;
+          h[0] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[0]) |
+                 ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[1]) << 16);
+          h[1] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[2]) |
+                 ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(h, xrsrc, xoff, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v[e]), xrsrc, xoff, 2 * e, 0);
+        }
       }
+      if (ACT == ACT_DGELU) {
+        unsigned short zb[4];
+        if (vec) {
+          const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(xrsrc, xoff, 0, 0);
+          zb[0] = (unsigned short)h[0];
+          zb[1] = (unsigned short)(h[0] >> 16);
+          zb[2] = (unsigned short)h[1];
+          zb[3] = (unsigned short)(h[1] >> 16);
+        } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = acc[im][jn][e];
-        const int erow = 8 * (e >> 2) + (e & 3);
-        if (ACT == ACT_GELU_SAVE)
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), xrsrc, xoff,
-                                                (uint32_t)erow * xrow_bytes, 0);
-        if (ACT == ACT_GELU || ACT == ACT_GELU_SAVE) v = gelu(v);
-        if (ACT == ACT_DGELU) v *= gelu_grad((float)__builtin_bit_cast(__bf16, zb[e]));
-        const uint32_t srow = (uint32_t)erow * row_bytes;
-        if (OUT == OUT_F32)  // fp32 results (partials) are streamed out (nontemporal): measured 6-15% faster
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), crsrc, voff, srow, kStoreNT);
-        else
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), crsrc, voff, srow, 0);
+          for (int e = 0; e < 4; ++e) zb[e] = __builtin_amdgcn_raw_buffer_load_b16(xrsrc, xoff, 2 * e, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= gelu_grad((float)__builtin_bit_cast(__bf16, zb[e]));
+      }
+      if (ACT == ACT_GELU || ACT == ACT_GELU_SAVE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = gelu(v[e]);
+      }
+      if (OUT == OUT_F32) {  // fp32 results (partials) are streamed out (nontemporal): measured 6-15% faster
+        if (vec) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crsrc, voff, 0, kStoreNT);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[e]), crsrc, voff, 4 * e, kStoreNT);
+        }
+      } else {
+        if (vec) {
+          u32x2 h;
+          h[0] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[0]) |
+                 ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[1]) << 16);
+          h[1] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[2]) |
+                 ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)v[3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(h, crsrc, voff, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v[e]), crsrc, voff, 2 * e, 0);
+        }
       }
     }
   }
 }
 
 // Main-loop schedules.
-//   SCHED_PLAIN: every wave reads the next 16-wide k step's fragments while
+//   SCHED_PLAIN: every wave reads the next 32-deep k step's fragments while
 //     its matrix cores work on the current one; one barrier per k-tile.
 //   SCHED_WEAVE: the same, with the reads and MFMAs interleaved two MFMAs at
 //     a time by scheduling-group barriers.
 //   SCHED_PINGPONG: the two waves that share a SIMD (waves w and w + 4) run
 //     one phase apart. In a memory phase a wave reads all fragments of one
 //     k-tile from LDS into registers and issues its share of the HBM->LDS
-//     loads; in a compute phase it issues the k-tile's 32 MFMAs from
+//     loads; in a compute phase it issues the k-tile's 64 MFMAs from
 //     registers with nothing in between. Barriers separate the phases, so at
 //     any time one wave of each SIMD feeds the matrix cores and the other
 //     moves data.
+// The launches use SCHED_PINGPONG; the other two remain for timing
+// comparisons (TP_GEMM_SCHED).
 enum Sched : int { SCHED_PLAIN = 0, SCHED_WEAVE = 1, SCHED_PINGPONG = 2 };
 
 // s_waitcnt immediates (vmcnt, expcnt, lgkmcnt fields of the gfx9 encoding; a field at its
@@ -334,7 +400,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
 
   Frags<A_KROWS, FM> ra;
   Frags<B_KROWS, FN> rb;
-  // LDS reads per 16-wide k step: one b128 per K-rows fragment, two transpose reads per MN-rows one
+  // LDS reads per 32-deep k step: one b128 per K-rows fragment, two transpose reads per MN-rows one
   constexpr int kReads = (A_KROWS ? FM : 2 * FM) + (B_KROWS ? FN : 2 * FN);
   ra.init(lane, wm * WM);
   rb.init(lane, wn * WN);
@@ -344,13 +410,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
     rb.read(b, kk, lane, fb[slot]);
   };
 
-  f32x16 acc[FM][FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int jn = 0; jn < FN; ++jn)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][jn][e] = 0.f;
 
   if constexpr (SCHED == SCHED_PINGPONG) {
     // Phases are numbered by the barriers between them. Group 0 (waves 0..3)
@@ -362,10 +428,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
     // loads at the end of the next phase, before the barrier after which
     // k-tile i + 2 is first read.
     const int grp = wave >> 2;
-    bf16x8 ta[BK / 16][FM], tb[BK / 16][FN];
+    bf16x8 ta[BK / KS][FM], tb[BK / KS][FN];
     auto read_tile = [&](const char* a, const char* b) {
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int kk = 0; kk < BK / KS; ++kk) {
         ra.read(a, kk, lane, ta[kk]);
         rb.read(b, kk, lane, tb[kk]);
       }
@@ -373,12 +439,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
     auto mma_tile = [&]() {
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk)
+      for (int kk = 0; kk < BK / KS; ++kk)
 #pragma unroll
         for (int im = 0; im < FM; ++im)
 #pragma unroll
           for (int jn = 0; jn < FN; ++jn)
-            acc[im][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[kk][im], tb[kk][jn], acc[im][jn], 0, 0, 0);
+            acc[im][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta[kk][im], tb[kk][jn], acc[im][jn], 0, 0, 0);
       __builtin_amdgcn_s_setprio(0);
     };
     // group 0, k-tile i from stage (ca, cb); the other stage (na, nb) receives k-tile i + 1
@@ -422,25 +488,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
     }
   } else {
   // One k-tile: start the next tile's loads into the other stage, multiply the
-  // current stage 16 k at a time while reading the next fragments, then wait
+  // current stage 32 k at a time while reading the next fragments, then wait
   // for the next stage at the barrier and read its first fragments.
   auto iteration = [&](int kt, const char* ca, const char* cb, char* na, char* nb) {
     if (kt + 1 < KT) issue_loads(kt + 1, na, nb);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) read_frags(ca, cb, kk + 1, (kk + 1) & 1);
+    for (int kk = 0; kk < BK / KS; ++kk) {
+      if (kk + 1 < BK / KS) read_frags(ca, cb, kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int im = 0; im < FM; ++im)
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn)
-          acc[im][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][im], fb[kk & 1][jn], acc[im][jn], 0, 0, 0);
+          acc[im][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk & 1][im], fb[kk & 1][jn], acc[im][jn], 0, 0, 0);
       // WEAVE: interleave the next step's fragment reads with this step's
       // MFMAs, two MFMAs at a time, so every read has MFMAs to hide behind
       // (left alone, the compiler issues each read right before the MFMA that
       // needs it). Measured 3-6% faster for K up to 6144, 1-3% slower for
       // K of 8192 and more, where the kernels run long enough for the
       // engine clock to settle lower under the busier matrix cores.
-      if (SCHED == SCHED_WEAVE && kk + 1 < BK / 16) {
+      if (SCHED == SCHED_WEAVE && kk + 1 < BK / KS) {
         constexpr int r0 = kReads / 4, r1 = kReads * 2 / 4 - r0, r2 = kReads * 3 / 4 - r0 - r1;
         constexpr int r3 = kReads - r0 - r1 - r2, m = FM * FN / 4;
         __builtin_amdgcn_sched_group_barrier(0x100, r0, 0);
@@ -468,10 +534,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_mfma_kernel(Params p) {
   }
   }  // SCHED_PLAIN, SCHED_WEAVE
 
-  store_tile<OUT, ACT>(d, acc, m0, n0, z, lane, wm, wn);
+  // the stages are free once every wave is past its last fragment read
+  __syncthreads();
+  char* stage_of_wave = (wave >> 1) == 0 ? sA0 : (wave >> 1) == 1 ? sA1 : (wave >> 1) == 2 ? sB0 : sB1;
+  store_tile<OUT, ACT>(d, acc, m0, n0, z, lane, wm, wn, reinterpret_cast<float*>(stage_of_wave + (wave & 1) * 16384),
+                       p.vec);
 }
-
-constexpr int64_t kWeaveMaxK = 6144;
 
 // Schedule override for timing comparisons of the same product: TP_GEMM_SCHED = plain | weave | pingpong.
 int sched_override() {
@@ -488,18 +556,16 @@ int sched_override() {
 
 template <int OUT, int ACT, bool AT, bool BT>
 void launch_one(const Params& p, hipStream_t s) {
-  // Measured on the MLP and attention-projection shapes: the woven schedule
-  // is fastest up to K = 6144 (3-6%), the ping-pong one beyond (2-5%). With a
-  // transposed B the ping-pong kernel does not fit its registers (it would
-  // spill), so that case keeps the plain schedule.
-  int sched = p.d.K <= kWeaveMaxK ? SCHED_WEAVE : (BT ? SCHED_PLAIN : SCHED_PINGPONG);
+  // Measured on the MLP and attention-projection shapes (same process, one
+  // box): with the 16 x 16 x 32 MFMAs the ping-pong schedule is the fastest
+  // at every K, 3-7% ahead of the previous 32 x 32 x 16 kernels; the woven
+  // and plain schedules trail it by 5-20%.
+  int sched = SCHED_PINGPONG;
   if (sched_override() >= 0) sched = sched_override();
   const dim3 grid((unsigned)p.total), block(NTHREADS);
-  if constexpr (!BT) {
-    if (sched == SCHED_PINGPONG) {
-      gemm_bf16_mfma_kernel<OUT, ACT, AT, BT, SCHED_PINGPONG><<<grid, block, 0, s>>>(p);
-      return;
-    }
+  if (sched == SCHED_PINGPONG) {
+    gemm_bf16_mfma_kernel<OUT, ACT, AT, BT, SCHED_PINGPONG><<<grid, block, 0, s>>>(p);
+    return;
   }
   if (sched == SCHED_WEAVE)
     gemm_bf16_mfma_kernel<OUT, ACT, AT, BT, SCHED_WEAVE><<<grid, block, 0, s>>>(p);
@@ -536,6 +602,13 @@ hipError_t launch_gemm_mfma(const GemmDesc& d, hipStream_t stream) {
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
   p.total = (int)total;
+  {
+    const int64_t es = d.out_kind == OUT_F32 ? 4 : 2;
+    bool v = (reinterpret_cast<uintptr_t>(d.C) % (4 * es)) == 0 && d.ldc % 4 == 0 && d.sC % 4 == 0;
+    if (d.act == ACT_GELU_SAVE || d.act == ACT_DGELU)
+      v = v && (reinterpret_cast<uintptr_t>(d.aux) % 8) == 0 && d.ldx % 4 == 0 && d.sX % 4 == 0;
+    p.vec = v ? 1 : 0;
+  }
   const bool f32 = d.out_kind == OUT_F32;
   if (!d.a_trans && !d.b_trans) {
     // forward products
