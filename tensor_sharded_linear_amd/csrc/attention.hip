@@ -76,10 +76,14 @@ struct AttnParams {
 // max(v of lane l, v of lane l ^ 32): the two halves of the wave are exchanged in registers
 // (v_permlane32_swap: the upper half of one copy trades places with the lower half of the other,
 // so each lane ends up holding both values of its pair).
+// The two halves are copied out of the returned pair before the bit casts: a
+// bit cast applied to an element of a vector value was compiled as a cast of
+// element 0.
 __device__ __forceinline__ float pair_max(float v) {
   const unsigned u = __builtin_bit_cast(unsigned, v);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  const unsigned lo = r[0], hi = r[1];
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
 }
 
 template <int DH>

@@ -298,8 +298,10 @@ __device__ __forceinline__ void store_tile(const GemmDesc& d, const AccTile& acc
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crsrc, voff, 0, kStoreNT);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[e]), crsrc, voff, 4 * e, kStoreNT);
+          for (int e = 0; e < 4; ++e) {
+            const float ve = v[e];  // a bit cast of v[e] itself was compiled as one of v[0]
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ve), crsrc, voff, 4 * e, kStoreNT);
+          }
         }
       } else {
         if (vec) {

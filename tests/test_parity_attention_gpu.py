@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import tensor_sharded_linear_amd as tp
-from synthetic import WORKLOADS, normal_bf16
+from synthetic import WORKLOADS, bf16_bits_from_f32, f32_from_bf16_bits, normal_bf16, rng
 from parity import assert_close, bf16_tensor, dev, f32_tensor, host, note
 
 pytestmark = pytest.mark.gpu
@@ -69,6 +69,31 @@ def test_attention_subset_partitioned_and_head_split():
     got = host(tp.attention(part, n, heads, kv_heads, dh, L, s0=1, ns=2, partitioned=True))
     ref = oracle.attention(qkv_vals[:, blk:3 * blk], n, heads, kv_heads, dh, L, True, 1, 2)
     assert_close(np.concatenate(list(got), axis=1), ref, "subset partitioned", stored_bf16=True)
+
+
+@pytest.mark.parametrize("big", [(4, 5, 6, 7), (0, 1, 2, 3)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_scores_far_apart_within_a_key_block(big, causal):
+    """Keys at positions big (mod 8) score about 136 above the rest (natural-log units), so an
+    offset other than the true row max would overflow exp. The kernel splits each 64-key block's
+    scores of one query over two lanes in groups of 4 keys; both placements put the large scores
+    on one side of that split."""
+    dh, L = 128, 256
+    g = rng(2400, 0)
+    u = g.standard_normal(dh)
+    q = 3.0 * u + 0.05 * g.standard_normal((L, dh))
+    k = 0.05 * g.standard_normal((L, dh))
+    rows = np.array([j for j in range(L) if j % 8 in big])
+    k[rows] = 4.0 * u
+    v = g.standard_normal((L, dh))
+    bits = bf16_bits_from_f32(np.concatenate([q, k, v], axis=1).astype(np.float32))
+    vals = f32_from_bf16_bits(bits).astype(np.float64)
+    scores = vals[:, :dh] @ vals[:, dh:2 * dh].T / np.sqrt(dh)
+    assert scores[:, rows].min() - np.delete(scores, rows, axis=1).max() > 100.0
+    note(f"attention, scores far apart within a key block, big={big} causal={causal}")
+    got = host(tp.attention(bf16_tensor(bits), 1, 1, 1, dh, L, causal))
+    assert np.isfinite(got).all()
+    assert_close(got, oracle.attention(vals, 1, 1, 1, dh, L, causal), "attention, far-apart scores", stored_bf16=True)
 
 
 def test_attention_elementwise_path():

@@ -156,6 +156,26 @@ def test_mlp_backward_gelu(M, d, F, N, s0, ns):
     assert_close(host(dW2), r2, "dW2")
 
 
+def test_mlp_backward_workspace_off_the_vector_alignment():
+    """A workspace 4 bytes past an aligned address: the recomputed pre-activation and the GeLU'
+    product keep the large-tile kernel but store (and read) their workspace matrices one value
+    at a time; the products that read workspace matrices as operands take the guarded kernel."""
+    M, d, F, N = 300, 256, 1024, 2
+    xb, x = normal_bf16((M, d), 1.0, 1190, 0)
+    w1b, w1 = normal_bf16((d, F), 0.02, 1190, 1)
+    w2b, w2 = normal_bf16((F, d), 0.02, 1190, 2)
+    yb, dy = normal_bf16((M, d), 1.0, 1190, 3)
+    X, W1, W2, dY = bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), bf16_tensor(yb)
+    need = tp.mlp_backward_workspace_bytes(X, W1, W2, dY, N)
+    ws = torch.empty(need + 4, dtype=torch.uint8, device=dev())[4:]
+    note("mlp backward, workspace 4 bytes past alignment")
+    dX, dW1, dW2 = tp.mlp_backward(X, W1, W2, dY, N, workspace=ws)
+    rx, r1, r2 = oracle.mlp_backward(x, w1, w2, dy, N, "gelu")
+    assert_close(host(dX), rx, "dX")
+    assert_close(host(dW1), r1, "dW1")
+    assert_close(host(dW2), r2, "dW2")
+
+
 def test_mlp_backward_partial_outputs_and_fp32():
     M, d, F, N = 128, 64, 256, 2
     xb, x = normal_bf16((M, d), 1.0, 1600, 0)

@@ -187,6 +187,35 @@ def test_generic_path_unaligned_strides():
     assert_exact(host(tp.reduce_partials(P)), oracle.row_linear(xi, wi, 4), "generic row exact")
 
 
+def test_large_tile_kernel_with_unaligned_outputs():
+    """Outputs whose row stride or base address rule out 16-byte (fp32) or 8-byte (bf16) stores
+    still run on the large-tile kernel, which then stores each value alone."""
+    M, K, width, N = 300, 512, 264, 2
+    xb, x = normal_bf16((M, K), 1.0, 510, 0)
+    wb, w = normal_bf16((K, width * N), 0.02, 510, 1)
+    X, W = bf16_tensor(xb), bf16_tensor(wb)
+    ref = oracle.col_linear(x, w, N, "gelu")
+    note("large-tile col, bf16 Y with a row stride of 2 mod 4 elements")
+    Ybig = torch.zeros((M, width * N + 2), dtype=torch.bfloat16, device=dev())
+    got = tp.col_linear(X, W, N, act="gelu", out=Ybig[:, : width * N])
+    assert_close(host(got), ref, "col, bf16 Y stride 2 mod 4", stored_bf16=True)
+    assert torch.count_nonzero(Ybig[:, width * N:]) == 0
+    note("large-tile col, fp32 Y one element past a 16-byte boundary")
+    Yf = torch.zeros(M * width * N + 1, dtype=torch.float32, device=dev())
+    got = tp.col_linear(X, W, N, act="gelu", out=Yf[1:].view(M, width * N))
+    assert_close(host(got), ref, "col, fp32 Y offset by one element")
+    assert float(Yf[0]) == 0.0
+    note("large-tile row partials with an odd row stride")
+    hb, h = normal_bf16((M, 2 * K), 1.0, 511, 0)
+    w2b, w2 = normal_bf16((2 * K, width), 0.02, 511, 1)
+    Pbig = torch.zeros((2, M, width + 1), dtype=torch.float32, device=dev())
+    P = tp.row_linear(bf16_tensor(hb), bf16_tensor(w2b), 2, out=Pbig[:, :, :width])
+    parts = oracle.row_partials(h, w2, 2)
+    for j in range(2):
+        assert_close(host(P[j]), parts[j], f"row partial {j}, odd row stride")
+    assert torch.count_nonzero(Pbig[:, :, width:]) == 0
+
+
 def test_row_strides_past_31_bits_take_the_guarded_path():
     """Row strides whose 256-row tile span reaches 2^31 bytes leave the large-tile kernel (its
     buffer offsets are 31-bit) for the element-guarded one, which addresses in 64 bits."""
