@@ -81,14 +81,22 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // XOR swizzles of 16-byte chunks that keep the fragment reads free of bank
-// conflicts: K-rows tiles hold 8 chunks per row, MN-rows tiles 32. In an
-// MN-rows tile the four k-rows one transpose read takes (k-row bits 0-1) and
-// the two 16-lane groups read in the same cycle (k-rows 8 apart, bit 3) land
-// on distinct slots.
+// conflicts: K-rows tiles hold 8 chunks per row, MN-rows tiles 32. The LDS
+// serves a 16-byte read to lanes 8i .. 8i + 7 together with lanes 32 + 8i ..
+// 32 + 8i + 7, and an 8-byte transpose read to 32 consecutive lanes (bank
+// conflict counters: zero with these layouts). In an MN-rows tile the four
+// k-rows one transpose read takes (k-row bits 0-1) and the two 16-lane groups
+// served together (k-rows 16 apart, bit 4) land on distinct slots.
 __device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int swz_mn(int krow) {
-  return ((krow & 1) * 6) ^ (((krow >> 1) & 1) * 12) ^ (((krow >> 3) & 1) * 2);
+  return ((krow & 1) * 6) ^ (((krow >> 1) & 1) * 12) ^ (((krow >> 4) & 1) * 2);
 }
+
+// The 8-wide k chunk of a 32-deep k step that lane group G = lane / 16 holds
+// in both MFMA operands. Any assignment gives the same product; this one puts
+// chunks c and c ^ 1 (not c and c ^ 2) on the lanes a 16-byte read serves
+// together, which the K-rows swizzle separates.
+__device__ __forceinline__ int kgroup_chunk(int G) { return ((G & 1) << 1) | (G >> 1); }
 
 // One operand of the product: where its tile comes from and how it is laid out.
 // KROWS: the operand is stored with k contiguous (A [M, K] or B [N, K]).
@@ -98,6 +106,7 @@ struct Operand {
   int64_t ld;          // row stride of the stored matrix, elements
   int extent;          // rows (KROWS) or columns (MN-rows) of the tile inside the matrix
   uint32_t voff, srow;
+  uint32_t voff_odd;   // MN-rows: the offset for regions w + 8 i with i odd
   int kc;              // KROWS: the k chunk this lane loads
 
   __device__ __forceinline__ void init(int lane, int wave) {
@@ -109,9 +118,11 @@ struct Operand {
       srow = (uint32_t)(8 * ld * 2);
     } else {
       // region r = k-rows 2r, 2r+1; lane l -> k-row + (l >> 5), slot l & 31,
-      // chunk (l & 31) ^ swz_mn(k-row), the same for regions w + 8 i
+      // chunk (l & 31) ^ swz_mn(k-row); for regions w + 8 i the k-row is
+      // 2 w + 16 i + (l >> 5), whose swizzle bits depend on i only through i % 2
       kc = 0;
       voff = (uint32_t)((lane >> 5) * ld * 2 + (((lane & 31) ^ swz_mn(2 * wave + (lane >> 5))) * 16));
+      voff_odd = (uint32_t)((lane >> 5) * ld * 2 + (((lane & 31) ^ swz_mn(2 * wave + 16 + (lane >> 5))) * 16));
       srow = (uint32_t)(2 * ld * 2);
     }
   }
@@ -131,33 +142,35 @@ struct Operand {
           make_rsrc(tile + (int64_t)k0 * ld, ((int64_t)(min(krem, BK) - 1) * ld + extent) * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TP_LDS(base + i * 8192), 16, voff, (wave + 8 * i) * srow, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TP_LDS(base + i * 8192), 16, (i & 1) ? voff_odd : voff,
+                                                 (wave + 8 * i) * srow, 0, 0);
     }
   }
 };
 
 // Fragment reads of F 16-wide blocks starting at row/col `pos` of the tile,
 // for the 32-deep k step kk of the tile. Either layout yields the lane format
-// both MFMA operands use: lane l holds row/col (l & 15) of the block and k
-// values 8 (l >> 4) .. + 7 of the k step.
+// both MFMA operands use: lane l holds row/col (l & 15) of the block and the
+// k values of chunk kgroup_chunk(l >> 4) of the k step.
 template <bool KROWS, int F>
 struct Frags {
   int off[F];
   __device__ __forceinline__ void init(int lane, int pos) {
     if (KROWS) {
-      // row pos + 16 f + (l & 15), k chunk 4 kk + (l >> 4); kk only flips bit 2 of the chunk
+      // row pos + 16 f + (l & 15), k chunk 4 kk + kgroup_chunk(l >> 4); kk only flips bit 2 of the chunk
+      const int kg = kgroup_chunk(lane >> 4);
 #pragma unroll
       for (int f = 0; f < F; ++f) {
         const int row = pos + f * 16 + (lane & 15);
-        off[f] = row * 128 + (((lane >> 4) ^ swz_k(row)) << 4);
+        off[f] = row * 128 + ((kg ^ swz_k(row)) << 4);
       }
     } else {
       // transpose reads: lane (G = lane >> 4, j = lane & 15) supplies k-row
-      // 32 kk + 8 G + 4 t + (j >> 2) and columns 4 (j & 3) .. + 3 of a 16-wide
-      // block, and receives 4 k values of column j; t and kk leave the k-row
-      // bits the swizzle uses unchanged
+      // 32 kk + 8 kgroup_chunk(G) + 4 t + (j >> 2) and columns 4 (j & 3) .. + 3
+      // of a 16-wide block, and receives 4 k values of column j; t and kk leave
+      // the k-row bits the swizzle uses unchanged
       const int G = lane >> 4, j16 = lane & 15;
-      const int kr = 8 * G + (j16 >> 2);
+      const int kr = 8 * kgroup_chunk(G) + (j16 >> 2);
       const int sw = swz_mn(kr);
 #pragma unroll
       for (int f = 0; f < F; ++f) {
