@@ -216,6 +216,24 @@ def test_large_tile_kernel_with_unaligned_outputs():
     assert torch.count_nonzero(Pbig[:, :, width:]) == 0
 
 
+def test_long_k_shorter_tile_groups_with_ragged_tiles():
+    """K long enough (10496) that the large-tile kernel groups tiles 2 rows tall, with 3 row tiles
+    (the last group 1 row tall) and a ragged column tile, for both splits."""
+    M, K, width, N = 600, 10496, 264, 2
+    xb, x = normal_bf16((M, K), 1.0, 520, 0)
+    wb, w = normal_bf16((K, width * N), 0.02, 520, 1)
+    note("long K: col, GeLU, 3 row tiles, ragged columns")
+    got = host(tp.col_linear(bf16_tensor(xb), bf16_tensor(wb), N, act="gelu", out_dtype=torch.float32))
+    assert_close(got, oracle.col_linear(x, w, N, "gelu"), "long-K col")
+    hb, h = normal_bf16((M, K * N), 1.0, 521, 0)
+    w2b, w2 = normal_bf16((K * N, width), 0.02, 521, 1)
+    note("long K: row partials, 3 row tiles, ragged columns")
+    P = tp.row_linear(bf16_tensor(hb), bf16_tensor(w2b), N)
+    parts = oracle.row_partials(h, w2, N)
+    for j in range(N):
+        assert_close(host(P[j]), parts[j], f"long-K row partial {j}")
+
+
 def test_row_strides_past_31_bits_take_the_guarded_path():
     """Row strides whose 256-row tile span reaches 2^31 bytes leave the large-tile kernel (its
     buffer offsets are 31-bit) for the element-guarded one, which addresses in 64 bits."""
