@@ -244,6 +244,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], c, -mc));
       float lsum = 0.f;
+      // The two waves that share a SIMD come from different workgroups and run
+      // unsynchronized; while this wave feeds the value product it takes issue
+      // priority, so the other wave's softmax work fills the MFMA gaps rather
+      // than delaying the MFMAs (measured 1-3% faster than equal priority;
+      // raising it around the score MFMAs as well gained nothing).
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
       // O^T += V^T P^T, 16 keys per step; step t takes elements 8 (t % 2) .. + 7 of tile t / 2,
       // i.e. keys 16 t + 8 (i / 4) + 4 hh + i % 4 for i = 0..7 (the k order of this step).
       // Each fp32 probability p is carried as two bf16 values, hi = bf16(p) and
@@ -277,6 +284,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, o[dt], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       l_run += lsum;
     };
 
