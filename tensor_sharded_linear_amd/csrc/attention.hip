@@ -43,6 +43,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
@@ -261,12 +263,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_mfma_kernel(AttnParams 
       for (int t = 0; t < 4; ++t) {
         bf16x8 pf, pl;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pv = s[t >> 1][8 * (t & 1) + i];
-          const __bf16 hi = (__bf16)pv;
-          pf[i] = hi;
-          pl[i] = (__bf16)(pv - (float)hi);
-          lsum += pv;
+        for (int i = 0; i < 8; i += 2) {  // two probabilities per conversion instruction
+          const f32x2 pv = {s[t >> 1][8 * (t & 1) + i], s[t >> 1][8 * (t & 1) + i + 1]};
+          const bf16x2 hi = __builtin_convertvector(pv, bf16x2);
+          const bf16x2 lo = __builtin_convertvector(pv - __builtin_convertvector(hi, f32x2), bf16x2);
+          pf[i] = hi[0];
+          pf[i + 1] = hi[1];
+          pl[i] = lo[0];
+          pl[i + 1] = lo[1];
+          lsum += pv[0];
+          lsum += pv[1];
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
