@@ -2,17 +2,17 @@
 // C_z = act(A_z B_z) with M <= 32, fp32 accumulate, on the gfx950 matrix cores.
 //
 // With so few rows the product is bound by streaming B (the weight shard)
-// from HBM exactly once, so the kernel is built for bytes in flight and high
-// occupancy, with no workgroup barrier in its main loop. A workgroup of 8
-// waves owns SBN = 128 or 256 columns of one shard (and a chunk of K when K is
-// split); each wave walks every 8th 32-row slice of that chunk on its own. A
-// slice of B (32 x SBN bf16, 8 or 16 KB) comes into registers with 16-byte
-// nontemporal buffer loads, one or two slices ahead, goes through the wave's
-// private patch of LDS so that
-// ds_read_b64_tr_b16 can hand out K-contiguous fragments, and meets the A
-// fragment (the 16 or 32 token rows, loaded straight from global memory) in
+// from HBM exactly once, so the kernel is built for bytes in flight, with no
+// workgroup barrier in its main loop. A workgroup of 4 waves owns SBN = 128
+// or 256 columns of one shard (and a chunk of K when K is split); each wave
+// walks every 4th 32-row slice of that chunk on its own. A slice of B
+// (32 x SBN bf16, 8 or 16 KB) goes straight from HBM into one of the wave's
+// own LDS buffers with 16-byte nontemporal LDS-mode buffer loads, 4 (128
+// columns) or 2 (256 columns) slices ahead, so that ds_read_b64_tr_b16 can
+// hand out K-contiguous fragments, and meets the A fragment (the 16 or 32
+// token rows, loaded straight from global memory) in
 // v_mfma_f32_16x16x32_bf16 with the token rows as the M dimension. At the end
-// the 8 waves' sums are added in wave order through LDS. Splitting K over
+// the 4 waves' sums are added in wave order through LDS. Splitting K over
 // workgroups (ksplit > 1) leaves fp32 chunk sums that skinny_finish_kernel
 // adds in ascending chunk order.
 //
@@ -32,25 +32,31 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
 constexpr int SLICE = 32;      // k-rows per wave step
-constexpr int NWAVES = 8;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr int SBK = SLICE * NWAVES;  // K-chunks are multiples of this
+constexpr int SBK_MAX = 256;   // K-chunks are whole multiples of 256 rows (of SLICE x waves = 128)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kStream = 2;  // buffer-load cache policy: nontemporal (the weights are read once)
+#define TP_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Column-tile geometry. Wider tiles read longer contiguous pieces of each
 // weight row per request wave, which keeps HBM pages open longer: on the
 // decode shapes each doubling of the width up to 256 measured 6-13% faster,
-// as long as there are enough tiles to give most CUs one.
+// as long as there are enough tiles to give most CUs one. 4 waves, each with
+// NBUF slice buffers: 4 x 8 KB for 128 columns, 2 x 16 KB for 256, so 128 KB
+// of LDS and one workgroup per CU either way. Measured on the decode shapes,
+// 4 waves beat 8 waves with 2 slices each (128 columns) and 2 waves with 4
+// slices each (256 columns).
 template <int SBN>
 struct Tile {
   static_assert(SBN == 128 || SBN == 256, "tile width");
-  static constexpr int CPR = SBN / 8;             // 16-byte chunks per B row
-  static constexpr int LPL = SLICE * CPR / 64;    // B loads per lane per slice
-  static constexpr int NSUB = SBN / 16;           // 16-column MFMA subtiles
-  static constexpr int UNROLL = 256 / SBN;        // slices of loads in flight per wave
-  static constexpr int PATCH = SLICE * SBN * 2;   // LDS per wave
+  static constexpr int CPR = SBN / 8;                 // 16-byte chunks per B row
+  static constexpr int NSUB = SBN / 16;               // 16-column MFMA subtiles
+  static constexpr int SLICE_BYTES = SLICE * SBN * 2;  // 8 or 16 KB
+  static constexpr int DMA = SLICE_BYTES / 1024;       // 1 KB LDS-mode loads per slice
+  static constexpr int RPD = 1024 / (SBN * 2);         // B rows per such load
+  static constexpr int NW = 4;                         // waves per workgroup
+  static constexpr int NBUF = SBN == 128 ? 4 : 2;      // slices of each wave in LDS, in flight together
+  static constexpr int SBK = SLICE * NW;               // K-chunk granule
 };
 
 struct SkParams {
@@ -72,18 +78,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // further on (the next 16-lane group) move to the other half of the window.
 __device__ __forceinline__ int swz_w(int r) { return (2 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
 
+// s_waitcnt immediates (vmcnt field of the gfx9 encoding; expcnt and lgkmcnt at their maximum)
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xC07F;
+
 template <int SBN, int MT, int OUT, int ACT, bool PARTIAL>
-__global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(SkParams p) {
+__global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParams p) {
   using T = Tile<SBN>;
-  constexpr int LPL = T::LPL, NSUB = T::NSUB, UNROLL = T::UNROLL, PATCH = T::PATCH, CPR = T::CPR;
-  // one staging patch per wave; reused for the cross-wave sum, 64 columns at a time
-  constexpr int RED_BYTES = NWAVES * MT * 16 * 64 * 4;
-  constexpr int LDS_BYTES = NWAVES * PATCH > RED_BYTES ? NWAVES * PATCH : RED_BYTES;
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  constexpr int NSUB = T::NSUB, CPR = T::CPR, DMA = T::DMA, RPD = T::RPD, NW = T::NW;
+  constexpr int SLICE_BYTES = T::SLICE_BYTES;
+  constexpr int NBUF = T::NBUF;
+  // NBUF slice buffers per wave, each buffer index its own array so the
+  // compiler can tell the buffers being filled by LDS-mode loads from the one
+  // being read; the first also takes the cross-wave sum at the end
+  // (NW x MT x 16 x 64 floats).
+  static_assert(NW * MT * 16 * 64 * 4 <= NW * SLICE_BYTES, "reduction space");
+  __shared__ __attribute__((aligned(1024))) char lds0[NW * SLICE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds1[NW * SLICE_BYTES];
   const GemmDesc& d = p.d;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  char* patch = lds + wave * PATCH;
+  char* buf0 = lds0 + wave * SLICE_BYTES;
+  char* buf1 = lds1 + wave * SLICE_BYTES;
   const int64_t n0 = (int64_t)blockIdx.x * SBN;
   const int z = blockIdx.y;
   const int c = blockIdx.z;
@@ -91,22 +107,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(SkParams p) {
   const int64_t kbeg = (int64_t)c * p.kchunk;
   const int64_t kend = min(K, kbeg + p.kchunk);
   const int nslices = kend > kbeg ? (int)((kend - kbeg + SLICE - 1) / SLICE) : 0;
-  const int nsteps = nslices > wave ? (nslices - wave + NWAVES - 1) / NWAVES : 0;  // slices wave, wave + 8, ...
+  const int nsteps = nslices > wave ? (nslices - wave + NW - 1) / NW : 0;  // slices wave, wave + NW, ...
 
   const __bf16* Az = static_cast<const __bf16*>(d.A) + z * d.sA;
   const __bf16* Bz = static_cast<const __bf16*>(d.B) + z * d.sB + n0;
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Az, ((M - 1) * lda + K) * 2);
 
-  // B slice loads: chunk q = lane + 64 i -> k-row q / CPR, column chunk q % CPR.
-  uint32_t w_voff[LPL];
-  int w_lds[LPL];
+  // LDS-mode load i of a slice writes 1 KB at buffer offset 1024 i, lane l at
+  // +16 l: B row RPD i + l / CPR, slot l % CPR, so the lane fetches the chunk
+  // that slot holds under the swizzle.
+  uint32_t dma_voff[DMA];
 #pragma unroll
-  for (int i = 0; i < LPL; ++i) {
-    const int q = lane + 64 * i;
-    const int row = q / CPR, ch = q % CPR;
-    w_voff[i] = (uint32_t)(row * ldb * 2 + ch * 16);
-    w_lds[i] = row * (SBN * 2) + ((ch ^ swz_w(row)) << 4);
+  for (int i = 0; i < DMA; ++i) {
+    const int row = RPD * i + lane / CPR, slot = lane % CPR;
+    dma_voff[i] = (uint32_t)(row * ldb * 2 + ((slot ^ swz_w(row)) << 4));
   }
+  // captured through a pointer: the host compile pass rejects a lambda that
+  // captures a local array of template-dependent size
+  const uint32_t* const dvo = dma_voff;
   // A fragment: lane holds row (lane & 15) + 16 mt, 8 k-values at 8 (lane >> 4) of the slice.
   uint32_t x_voff[MT];
 #pragma unroll
@@ -129,45 +147,94 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(SkParams p) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[mt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = 0; s0 < nsteps; s0 += UNROLL) {
-    u32x4 wv[UNROLL][LPL], xv[UNROLL][MT];
+  // Slice i of this wave (k-rows kbeg + (wave + NW i) * 32 ..): B into LDS
+  // buffer `buf`, the token fragment into x. Rows past K fall outside the
+  // range and read as zero, like k chunks of A at or past K; a slice past the
+  // wave's share (i >= nsteps) takes an empty range and reads as zero whole.
+  u32x4 xv[NBUF][MT];
+  auto issue = [&](int i, char* buf, u32x4 (&x)[MT]) {
+    const bool valid = i < nsteps;
+    const int64_t k0 = kbeg + (int64_t)(wave + NW * i) * SLICE;
+    const int64_t krem = K - k0;
+    const int64_t bytes = valid ? ((min<int64_t>(krem, SLICE) - 1) * ldb + (N - n0)) * 2 : 0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(Bz + (valid ? k0 : 0) * ldb, bytes);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      if (s0 + u < nsteps) {
-        const int64_t k0 = kbeg + (int64_t)(wave + NWAVES * (s0 + u)) * SLICE;
-        const int64_t krem = K - k0;
-        const __amdgpu_buffer_rsrc_t wr =
-            make_rsrc(Bz + k0 * ldb, ((min<int64_t>(krem, SLICE) - 1) * ldb + (N - n0)) * 2);
+    for (int q = 0; q < DMA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, TP_LDS(buf + q * 1024), 16, dvo[q], 0, 0, kStream);
+    const uint32_t kk = (uint32_t)(k0 * 2);
 #pragma unroll
-        for (int i = 0; i < LPL; ++i) wv[u][i] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_voff[i], 0, kStream);
-        const uint32_t kk = (uint32_t)(k0 * 2);
+    for (int mt = 0; mt < MT; ++mt)
+      x[mt] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, valid && x_k < krem ? x_voff[mt] + kk : kOOB, 0, 0);
+  };
+  auto consume = [&](const char* buf, const u32x4 (&x)[MT]) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)  // k-chunks at or past K read as zero
-          xv[u][mt] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, x_k < krem ? x_voff[mt] + kk : kOOB, 0, 0);
-      }
+    for (int sub = 0; sub < NSUB; ++sub) {
+      // subtile sub adds 2 sub to the chunk index; the swizzle is an XOR
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(buf + (tr_off[0] ^ ((2 * sub) << 4))));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(buf + (tr_off[1] ^ ((2 * sub) << 4))));
+      const bf16x8 bfr = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[mt]), bfr, acc[mt][sub], 0, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      if (s0 + u < nsteps) {
-#pragma unroll
-        for (int i = 0; i < LPL; ++i) *reinterpret_cast<u32x4*>(patch + w_lds[i]) = wv[u][i];
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-          // subtile sub adds 2 sub to the chunk index; the swizzle is an XOR
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(patch + (tr_off[0] ^ ((2 * sub) << 4))));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(patch + (tr_off[1] ^ ((2 * sub) << 4))));
-          const bf16x8 bfr = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[mt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[u][mt]), bfr,
-                                                                   acc[mt][sub], 0, 0, 0);
-        }
-      }
+  };
+
+  // NBUF slices in flight per wave: a slice's buffer is refilled with the
+  // slice NBUF ahead as soon as its reads have returned, so the next NBUF - 1
+  // slices' loads are always on their way while one is multiplied. Loads
+  // complete in issue order: waiting until only the later slices' loads
+  // remain means this one has landed. No barrier: every buffer belongs to
+  // one wave. Issues and multiplications take no branch (past the share they
+  // move zeros), which keeps the compiler's own tracking of the LDS-mode
+  // loads exact.
+  constexpr int kPerSlice = DMA + MT;  // loads per slice issue
+  static_assert(NBUF == 2 || NBUF == 4, "ring depth");
+  static_assert((NBUF - 1) * kPerSlice <= 63, "vmcnt range");
+  if constexpr (NBUF == 4) {
+    __shared__ __attribute__((aligned(1024))) char lds2[NW * SLICE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds3[NW * SLICE_BYTES];
+    char* buf2 = lds2 + wave * SLICE_BYTES;
+    char* buf3 = lds3 + wave * SLICE_BYTES;
+    issue(0, buf0, xv[0]);
+    issue(1, buf1, xv[1]);
+    issue(2, buf2, xv[2]);
+    issue(3, buf3, xv[3]);
+    for (int i = 0; i < nsteps; i += 4) {
+      __builtin_amdgcn_s_waitcnt(wait_vm(3 * kPerSlice));
+      consume(buf0, xv[0]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue(i + 4, buf0, xv[0]);
+      __builtin_amdgcn_s_waitcnt(wait_vm(3 * kPerSlice));
+      consume(buf1, xv[1]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue(i + 5, buf1, xv[1]);
+      __builtin_amdgcn_s_waitcnt(wait_vm(3 * kPerSlice));
+      consume(buf2, xv[2]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue(i + 6, buf2, xv[2]);
+      __builtin_amdgcn_s_waitcnt(wait_vm(3 * kPerSlice));
+      consume(buf3, xv[3]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue(i + 7, buf3, xv[3]);
+    }
+  } else {
+    issue(0, buf0, xv[0]);
+    issue(1, buf1, xv[1]);
+    for (int i = 0; i < nsteps; i += 2) {
+      __builtin_amdgcn_s_waitcnt(wait_vm(kPerSlice));
+      consume(buf0, xv[0]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue(i + 2, buf0, xv[0]);
+      __builtin_amdgcn_s_waitcnt(wait_vm(kPerSlice));
+      consume(buf1, xv[1]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue(i + 3, buf1, xv[1]);
     }
   }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));  // the last issues may still be writing their zeros
 
-  // Add the 8 waves' sums in wave order through LDS, 64 columns at a time.
-  float* red = reinterpret_cast<float*>(lds);  // [8][MT * 16][64]
+  // Add the NW waves' sums in wave order through LDS, 64 columns at a time.
+  float* red = reinterpret_cast<float*>(lds0);  // [NW][MT * 16][64]
 #pragma unroll
   for (int cb = 0; cb < SBN / 64; ++cb) {
     __syncthreads();
@@ -181,10 +248,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_skinny_kernel(SkParams p) {
     __syncthreads();
     const int col = tid & 63;
     const int64_t gn = n0 + cb * 64 + col;
-    for (int row = tid >> 6; row < MT * 16; row += NWAVES) {
+    for (int row = tid >> 6; row < MT * 16; row += NW) {
       float v = red[row * 64 + col];
 #pragma unroll
-      for (int w = 1; w < NWAVES; ++w) v += red[(w * MT * 16 + row) * 64 + col];
+      for (int w = 1; w < NW; ++w) v += red[(w * MT * 16 + row) * 64 + col];
       if (row < M && gn < N) {
         if (PARTIAL) {
           p.part[(((int64_t)c * d.batch + z) * M + row) * N + gn] = v;
@@ -218,7 +285,7 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(GemmDesc d, int kspl
 
 template <int SBN, int MT, bool PARTIAL>
 void launch_mt(const SkParams& p, dim3 grid, hipStream_t s) {
-  const dim3 block(NTHREADS);
+  const dim3 block(Tile<SBN>::NW * 64);
   if (PARTIAL) {
     gemm_skinny_kernel<SBN, MT, OUT_F32, ACT_NONE, true><<<grid, block, 0, s>>>(p);
     return;
@@ -240,9 +307,10 @@ int tile_width(const GemmDesc& d) {
 }
 
 int64_t chunk_for(int64_t K, int ksplit) {
+  // a multiple of both tile widths' granules, so the split does not depend on the width
   int64_t kc = (K + ksplit - 1) / ksplit;
-  kc = (kc + SBK - 1) / SBK * SBK;
-  return kc > 0 ? kc : SBK;
+  kc = (kc + SBK_MAX - 1) / SBK_MAX * SBK_MAX;
+  return kc > 0 ? kc : SBK_MAX;
 }
 
 }  // namespace
@@ -252,7 +320,7 @@ bool gemm_skinny_supported(const GemmDesc& d) {
   if (d.a_trans || d.b_trans || (d.act != ACT_NONE && d.act != ACT_GELU)) return false;
   if ((d.K & 7) || (d.N & 7) || (d.lda & 7) || (d.ldb & 7) || (d.sA & 7) || (d.sB & 7)) return false;
   if ((reinterpret_cast<uintptr_t>(d.A) & 15) || (reinterpret_cast<uintptr_t>(d.B) & 15)) return false;
-  if ((int64_t)SBK * d.ldb * 2 >= (1ll << 31)) return false;
+  if ((int64_t)SLICE * d.ldb * 2 >= (1ll << 31)) return false;
   if (((d.M - 1) * d.lda + d.K) * 2 >= (1ll << 31)) return false;
   if (d.batch > 65535 || (d.N + 127) / 128 > 0x7fffffff) return false;
   return true;
@@ -265,7 +333,7 @@ int skinny_ksplit(const GemmDesc& d) {
   const int sbn = tile_width(d);
   const int64_t tiles = (d.N + sbn - 1) / sbn * d.batch;
   int64_t ks = tiles >= 160 ? 1 : 256 / (tiles > 0 ? tiles : 1);
-  const int64_t max_ks = (d.K + SBK - 1) / SBK;
+  const int64_t max_ks = (d.K + SBK_MAX - 1) / SBK_MAX;
   if (ks > max_ks) ks = max_ks;
   if (ks > 64) ks = 64;
   if (ks < 1) ks = 1;
