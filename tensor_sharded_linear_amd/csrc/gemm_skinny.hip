@@ -299,11 +299,18 @@ void launch_mt(const SkParams& p, dim3 grid, hipStream_t s) {
   }
 }
 
-// Tile width: 256 columns when that still gives most CUs a workgroup; 128
-// otherwise, and always for 17..32 rows (twice the accumulators).
-int tile_width(const GemmDesc& d) {
+// Tile width: 256 columns when that still gives most CUs a workgroup. When
+// the caller has room for K-chunk sums, also 256 columns with K split in two
+// when the 256-column tiles number 96..128, so that the split gives 192..256
+// workgroups: on the decode shape (112 such tiles) that ran about 1% faster
+// than 128-column tiles unsplit, the chunk-sum pass included. 128 otherwise,
+// and always for 17..32 rows (twice the accumulators).
+int tile_width(const GemmDesc& d, bool may_split) {
   if (d.M > 16) return 128;
-  return (d.N + 255) / 256 * d.batch >= 192 ? 256 : 128;
+  const int64_t t256 = (d.N + 255) / 256 * d.batch;
+  if (t256 >= 192) return 256;
+  if (may_split && t256 >= 96 && t256 <= 128) return 256;
+  return 128;
 }
 
 int64_t chunk_for(int64_t K, int ksplit) {
@@ -327,10 +334,10 @@ bool gemm_skinny_supported(const GemmDesc& d) {
 }
 
 int skinny_ksplit(const GemmDesc& d) {
-  // Split K only when the column tiles leave many CUs idle: the chunk sums
-  // cost a write, a read and a second launch, which measured slower than
-  // one workgroup on each of 7 of every 8 CUs.
-  const int sbn = tile_width(d);
+  // Split K only when the column tiles of the chosen width leave many CUs
+  // idle (fewer than 160 tiles): the chunk sums cost a write, a read and a
+  // second launch.
+  const int sbn = tile_width(d, true);
   const int64_t tiles = (d.N + sbn - 1) / sbn * d.batch;
   int64_t ks = tiles >= 160 ? 1 : 256 / (tiles > 0 ? tiles : 1);
   const int64_t max_ks = (d.K + SBK_MAX - 1) / SBK_MAX;
@@ -353,7 +360,7 @@ hipError_t launch_gemm_skinny(const GemmDesc& d, int ksplit, float* part, hipStr
   p.d = d;
   p.kchunk = chunk_for(d.K, ksplit);
   p.part = part;
-  const int sbn = tile_width(d);
+  const int sbn = tile_width(d, ksplit > 1);  // the width skinny_ksplit assumed when it split K
   const dim3 grid((unsigned)((d.N + sbn - 1) / sbn), (unsigned)d.batch, (unsigned)(ksplit > 1 ? ksplit : 1));
   const bool partial = ksplit > 1;
   if (d.M > 16) {

@@ -328,6 +328,31 @@ def test_skinny_wide_tiles_ragged():
     assert_close(got, oracle.col_linear(x2, w2, N, "gelu"), "skinny wide col gelu")
 
 
+def test_mlp_skinny_wide_tiles_split_k():
+    # Inside tp_mlp the first product may split K: with 96..128 column tiles of
+    # 256 (here 12 per shard x 8 shards, the last one ragged: 3000 columns) it
+    # takes 256-column tiles and two K chunks, the second one short (1000 rows
+    # in chunks of 512), whose sums the finishing pass adds before the GeLU.
+    M, d, width, N = 5, 1000, 3000, 8
+    xi, xf = ints_bf16((M, d), -1, 1, 730, 0)
+    # 128 nonzero columns of X in each K chunk: |H| <= 256, so H is exact in bf16
+    keep = np.zeros(d, dtype=bool)
+    keep[0:128] = keep[600:728] = True
+    xi[:, ~keep] = 0
+    xf[:, ~keep] = 0
+    w1i, w1f = ints_bf16((d, width * N), -1, 1, 730, 1)
+    w2i, w2f = ints_bf16((width * N, d), -1, 1, 730, 2)
+    note(f"mlp skinny split-K exact M={M} d={d} width={width} N={N}")
+    got = host(tp.mlp(bf16_tensor(xi), bf16_tensor(w1i), bf16_tensor(w2i), N, act="none"))
+    assert_exact(got, oracle.mlp(xf, w1f, w2f, N, "none"), "mlp skinny split-K exact")
+    xb, x = normal_bf16((M, d), 1.0, 731, 0)
+    w1b, w1 = normal_bf16((d, width * N), 0.02, 731, 1)
+    w2b, w2 = normal_bf16((width * N, d), 0.02, 731, 2)
+    note(f"mlp skinny split-K gelu M={M} d={d} width={width} N={N}")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), N))
+    assert_close(got, oracle.mlp(x, w1, w2, N, "gelu"), "mlp skinny split-K gelu")
+
+
 # ----------------------------------------------------------------------------- combine kernels
 
 
