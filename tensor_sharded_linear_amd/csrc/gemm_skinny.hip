@@ -14,7 +14,9 @@
 // v_mfma_f32_16x16x32_bf16 with the token rows as the M dimension. At the end
 // the 4 waves' sums are added in wave order through LDS. Splitting K over
 // workgroups (ksplit > 1) leaves fp32 chunk sums that skinny_finish_kernel
-// adds in ascending chunk order.
+// adds in ascending chunk order, or that the next skinny product adds, in the
+// same order and with the same activation and rounding, as it loads them for
+// its token fragments (the MLP's second product: no pass in between).
 //
 // The sharded layers follow the "Tensor Parallelism" topic page
 // (chipfoundryservices.com), sections "Column-Wise Parallelism" and
@@ -28,6 +30,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
@@ -63,6 +66,10 @@ struct SkParams {
   GemmDesc d;
   int64_t kchunk;
   float* part;
+  // Chunked A (AK > 0): A_z(m, k) = bf16(act_a(sum_c apart[c a_cs + z a_sz + m a_ld + k])),
+  // the c summed in ascending order: the unfinished first product of an MLP.
+  const float* apart;
+  int64_t a_cs, a_sz, a_ld;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -82,7 +89,11 @@ __device__ __forceinline__ int swz_w(int r) { return (2 * (r & 3)) ^ (8 * ((r >>
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kWaitLgkm0 = 0xC07F;
 
-template <int SBN, int MT, int OUT, int ACT, bool PARTIAL>
+// AK = 0: A is bf16 (d.A, row stride lda), grid (tiles, batch, chunks).
+// AK > 0: A is AK fp32 chunk sums in p.apart, finished on load with ACTA;
+// the grid is one-dimensional with the batch index fastest, so that with 8
+// shards every XCD works on one shard and reads only that shard's sums.
+template <int SBN, int MT, int OUT, int ACT, bool PARTIAL, int AK = 0, int ACTA = ACT_NONE>
 __global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParams p) {
   using T = Tile<SBN>;
   constexpr int NSUB = T::NSUB, CPR = T::CPR, DMA = T::DMA, RPD = T::RPD, NW = T::NW;
@@ -100,18 +111,30 @@ __global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParam
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   char* buf0 = lds0 + wave * SLICE_BYTES;
   char* buf1 = lds1 + wave * SLICE_BYTES;
-  const int64_t n0 = (int64_t)blockIdx.x * SBN;
-  const int z = blockIdx.y;
-  const int c = blockIdx.z;
+  const int tile = AK > 0 ? (int)(blockIdx.x / (unsigned)d.batch) : (int)blockIdx.x;
+  const int z = AK > 0 ? (int)(blockIdx.x % (unsigned)d.batch) : (int)blockIdx.y;
+  const int64_t n0 = (int64_t)tile * SBN;
+  const int c = AK > 0 ? 0 : (int)blockIdx.z;
   const int64_t M = d.M, N = d.N, K = d.K, lda = d.lda, ldb = d.ldb;
   const int64_t kbeg = (int64_t)c * p.kchunk;
   const int64_t kend = min(K, kbeg + p.kchunk);
   const int nslices = kend > kbeg ? (int)((kend - kbeg + SLICE - 1) / SLICE) : 0;
   const int nsteps = nslices > wave ? (nslices - wave + NW - 1) / NW : 0;  // slices wave, wave + NW, ...
 
-  const __bf16* Az = static_cast<const __bf16*>(d.A) + z * d.sA;
   const __bf16* Bz = static_cast<const __bf16*>(d.B) + z * d.sB + n0;
-  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Az, ((M - 1) * lda + K) * 2);
+  // A: one range (bf16 rows of stride lda), or one per chunk sum (fp32 rows
+  // of stride a_ld >= K): rows past M fall outside either way and read as zero.
+  constexpr int NA = AK > 0 ? AK : 1;
+  constexpr int ESZ = AK > 0 ? 4 : 2;
+  const int64_t alda = AK > 0 ? p.a_ld : lda;
+  __amdgpu_buffer_rsrc_t arsrc[NA];
+  if constexpr (AK > 0) {
+#pragma unroll
+    for (int q = 0; q < AK; ++q)
+      arsrc[q] = make_rsrc(p.apart + q * p.a_cs + z * p.a_sz, ((M - 1) * p.a_ld + K) * 4);
+  } else {
+    arsrc[0] = make_rsrc(static_cast<const __bf16*>(d.A) + z * d.sA, ((M - 1) * lda + K) * 2);
+  }
 
   // LDS-mode load i of a slice writes 1 KB at buffer offset 1024 i, lane l at
   // +16 l: B row RPD i + l / CPR, slot l % CPR, so the lane fetches the chunk
@@ -125,10 +148,12 @@ __global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParam
   // captured through a pointer: the host compile pass rejects a lambda that
   // captures a local array of template-dependent size
   const uint32_t* const dvo = dma_voff;
-  // A fragment: lane holds row (lane & 15) + 16 mt, 8 k-values at 8 (lane >> 4) of the slice.
+  // A fragment: lane holds row (lane & 15) + 16 mt, 8 k-values at 8 (lane >> 4)
+  // of the slice: one 16-byte load of bf16, or two per chunk sum of fp32.
+  constexpr int XL = AK > 0 ? 2 * AK : 1;  // A loads per slice and row block
   uint32_t x_voff[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) x_voff[mt] = (uint32_t)((((lane & 15) + 16 * mt) * lda + 8 * (lane >> 4)) * 2);
+  for (int mt = 0; mt < MT; ++mt) x_voff[mt] = (uint32_t)((((lane & 15) + 16 * mt) * alda + 8 * (lane >> 4)) * ESZ);
   const int x_k = 8 * (lane >> 4);
   // B fragment via transpose reads: 16-lane group G = lane >> 4 takes k-rows
   // 8 G + 4 t .. + 3 of the slice; lane j = lane & 15 supplies row + (j >> 2),
@@ -151,8 +176,8 @@ __global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParam
   // buffer `buf`, the token fragment into x. Rows past K fall outside the
   // range and read as zero, like k chunks of A at or past K; a slice past the
   // wave's share (i >= nsteps) takes an empty range and reads as zero whole.
-  u32x4 xv[NBUF][MT];
-  auto issue = [&](int i, char* buf, u32x4 (&x)[MT]) {
+  u32x4 xv[NBUF][MT][XL];
+  auto issue = [&](int i, char* buf, u32x4 (&x)[MT][XL]) {
     const bool valid = i < nsteps;
     const int64_t k0 = kbeg + (int64_t)(wave + NW * i) * SLICE;
     const int64_t krem = K - k0;
@@ -161,12 +186,36 @@ __global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParam
 #pragma unroll
     for (int q = 0; q < DMA; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, TP_LDS(buf + q * 1024), 16, dvo[q], 0, 0, kStream);
-    const uint32_t kk = (uint32_t)(k0 * 2);
+    const uint32_t kk = (uint32_t)(k0 * ESZ);
+    const bool xin = valid && x_k < krem;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      x[mt] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, valid && x_k < krem ? x_voff[mt] + kk : kOOB, 0, 0);
+#pragma unroll
+      for (int l = 0; l < XL; ++l)
+        x[mt][l] = __builtin_amdgcn_raw_buffer_load_b128(arsrc[l / 2], xin ? x_voff[mt] + kk + 16 * (l & 1) : kOOB, 0, 0);
   };
-  auto consume = [&](const char* buf, const u32x4 (&x)[MT]) {
+  auto consume = [&](const char* buf, const u32x4 (&x)[MT][XL]) {
+    // token fragments: bf16 as loaded, or the chunk sums added in ascending
+    // order, activated and rounded to bf16 (what the finishing pass would store)
+    bf16x8 af[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (AK > 0) {
+        f32x8 v = __builtin_shufflevector(__builtin_bit_cast(f32x4, x[mt][0]), __builtin_bit_cast(f32x4, x[mt][1]),
+                                          0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int q = 1; q < AK; ++q)
+          v += __builtin_shufflevector(__builtin_bit_cast(f32x4, x[mt][2 * q]),
+                                       __builtin_bit_cast(f32x4, x[mt][2 * q + 1]), 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (ACTA == ACT_GELU) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = gelu(v[e]);
+        }
+        af[mt] = __builtin_convertvector(v, bf16x8);
+      } else {
+        af[mt] = __builtin_bit_cast(bf16x8, x[mt][0]);
+      }
+    }
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       // subtile sub adds 2 sub to the chunk index; the swizzle is an XOR
@@ -175,7 +224,7 @@ __global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParam
       const bf16x8 bfr = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        acc[mt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[mt]), bfr, acc[mt][sub], 0, 0, 0);
+        acc[mt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr, acc[mt][sub], 0, 0, 0);
     }
   };
 
@@ -187,7 +236,7 @@ __global__ __launch_bounds__(Tile<SBN>::NW * 64) void gemm_skinny_kernel(SkParam
   // one wave. Issues and multiplications take no branch (past the share they
   // move zeros), which keeps the compiler's own tracking of the LDS-mode
   // loads exact.
-  constexpr int kPerSlice = DMA + MT;  // loads per slice issue
+  constexpr int kPerSlice = DMA + MT * XL;  // loads per slice issue
   static_assert(NBUF == 2 || NBUF == 4, "ring depth");
   static_assert((NBUF - 1) * kPerSlice <= 63, "vmcnt range");
   if constexpr (NBUF == 4) {
@@ -360,6 +409,8 @@ hipError_t launch_gemm_skinny(const GemmDesc& d, int ksplit, float* part, hipStr
   p.d = d;
   p.kchunk = chunk_for(d.K, ksplit);
   p.part = part;
+  p.apart = nullptr;
+  p.a_cs = p.a_sz = p.a_ld = 0;
   const int sbn = tile_width(d, ksplit > 1);  // the width skinny_ksplit assumed when it split K
   const dim3 grid((unsigned)((d.N + sbn - 1) / sbn), (unsigned)d.batch, (unsigned)(ksplit > 1 ? ksplit : 1));
   const bool partial = ksplit > 1;
@@ -372,6 +423,39 @@ hipError_t launch_gemm_skinny(const GemmDesc& d, int ksplit, float* part, hipStr
   } else {
     if (partial) launch_mt<128, 1, true>(p, grid, stream);
     else launch_mt<128, 1, false>(p, grid, stream);
+  }
+  return hipGetLastError();
+}
+
+bool gemm_skinny_chunked_a_supported(const GemmDesc& d, const ChunkedA& a) {
+  if (a.ksplit != kChunkedA || (a.act != ACT_NONE && a.act != ACT_GELU)) return false;
+  if (d.M > 16 || d.out_kind != OUT_F32 || d.act != ACT_NONE || !gemm_skinny_supported(d)) return false;
+  if (a.ld < d.K || (a.ld & 3) || (a.sz & 3) || (a.cs & 3) || (reinterpret_cast<uintptr_t>(a.part) & 15)) return false;
+  if ((16 * a.ld + d.K) * 4 >= (1ll << 31)) return false;  // 32-bit ranges and offsets of all 16 fragment rows
+  return (d.N + 127) / 128 * d.batch <= 0x7fffffff;
+}
+
+hipError_t launch_gemm_skinny_chunked_a(const GemmDesc& d, const ChunkedA& a, hipStream_t stream) {
+  if (d.M <= 0 || d.N <= 0 || d.batch <= 0) return hipSuccess;
+  if (!gemm_skinny_chunked_a_supported(d, a)) return hipErrorInvalidValue;
+  const int act_a = a.act;
+  SkParams p;
+  p.d = d;
+  p.kchunk = d.K;
+  p.part = nullptr;
+  p.apart = a.part;
+  p.a_cs = a.cs;
+  p.a_sz = a.sz;
+  p.a_ld = a.ld;
+  const int sbn = tile_width(d, false);
+  const dim3 grid((unsigned)((d.N + sbn - 1) / sbn * d.batch)), block(Tile<128>::NW * 64);
+  constexpr int AK = kChunkedA;
+  if (sbn == 256) {
+    if (act_a == ACT_GELU) gemm_skinny_kernel<256, 1, OUT_F32, ACT_NONE, false, AK, ACT_GELU><<<grid, block, 0, stream>>>(p);
+    else gemm_skinny_kernel<256, 1, OUT_F32, ACT_NONE, false, AK, ACT_NONE><<<grid, block, 0, stream>>>(p);
+  } else {
+    if (act_a == ACT_GELU) gemm_skinny_kernel<128, 1, OUT_F32, ACT_NONE, false, AK, ACT_GELU><<<grid, block, 0, stream>>>(p);
+    else gemm_skinny_kernel<128, 1, OUT_F32, ACT_NONE, false, AK, ACT_NONE><<<grid, block, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

@@ -544,15 +544,41 @@ tp_status tp_mlp(const tp_matrix* X, const tp_matrix* W1, const tp_matrix* W2, i
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  float* part = skinny1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + off_k) : nullptr;
+  // When the first product leaves K-chunk sums and the second is skinny too,
+  // the second adds the sums (ascending), applies the activation and rounds
+  // to bf16 as it loads its token fragments: the H it multiplies is bitwise
+  // the one the finishing pass would have stored, without that pass. The
+  // sums are laid out [chunk][z1][M][N1] for the first product's batch z1;
+  // the second product's A_z is H's columns z sA .. z sA + K - 1.
+  tp::ChunkedA ca;
+  std::memset(&ca, 0, sizeof(ca));
+  bool chunked_a = false;
+  if (skinny1 && ksplit > 1 && r2.g.in_bf16 && !r2.g.a_trans && r2.g.A == c1.g.C && r2.g.lda == c1.g.ldc &&
+      r2.g.M == c1.g.M && c1.g.out_kind == tp::OUT_BF16) {
+    ca.part = part;
+    ca.ksplit = ksplit;
+    ca.act = c1.g.act;
+    ca.ld = c1.g.N;
+    ca.cs = (int64_t)c1.g.batch * c1.g.M * c1.g.N;
+    if (c1.g.batch == r2.g.batch && c1.g.N == r2.g.K && r2.g.sA == c1.g.sC) {
+      ca.sz = c1.g.M * c1.g.N;  // shard z's sums are their own block
+      chunked_a = true;
+    } else if (c1.g.batch == 1 && (int64_t)(r2.g.batch - 1) * r2.g.sA + r2.g.K <= c1.g.N) {
+      ca.sz = r2.g.sA;  // one block holding every shard's columns
+      chunked_a = true;
+    }
+    chunked_a = chunked_a && r2.g.M <= tp::kSkinnyMaxRows && tp::gemm_skinny_chunked_a_supported(r2.g, ca);
+  }
   if (skinny1) {
-    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_k);
     e = tp::launch_gemm_skinny(c1.g, ksplit, part, s);
-    if (e == hipSuccess && ksplit > 1) e = tp::launch_skinny_finish(c1.g, ksplit, part, s);
+    if (e == hipSuccess && ksplit > 1 && !chunked_a) e = tp::launch_skinny_finish(c1.g, ksplit, part, s);
   } else {
     e = run_gemm(c1.g, s);
   }
   if (e != hipSuccess) return TP_ERR_HIP;
-  if ((e = run_gemm(r2.g, s)) != hipSuccess) return TP_ERR_HIP;
+  e = chunked_a ? tp::launch_gemm_skinny_chunked_a(r2.g, ca, s) : run_gemm(r2.g, s);
+  if (e != hipSuccess) return TP_ERR_HIP;
   if (ns > 1) {
     CombineDesc cd;
     std::memset(&cd, 0, sizeof(cd));

@@ -114,6 +114,20 @@ size_t skinny_partial_bytes(const GemmDesc& d, int ksplit);
 hipError_t launch_gemm_skinny(const GemmDesc& d, int ksplit, float* part, hipStream_t stream);
 // C_z = act(sum_c part[c][z]) for the ksplit chunk sums written above.
 hipError_t launch_skinny_finish(const GemmDesc& d, int ksplit, const float* part, hipStream_t stream);
+// The next skinny product reading such chunk sums directly as its A operand:
+// C_z = A'_z B_z with A'_z(m, k) = bf16(act(sum_c part[c cs + z sz + m ld + k])),
+// c in ascending order, exactly what launch_skinny_finish would have stored
+// for A. Taken for kChunkedA chunks, M <= 16, fp32 output and no epilogue
+// activation of its own (d.A is not read).
+constexpr int kChunkedA = 2;
+struct ChunkedA {
+  const float* part;
+  int64_t cs, sz, ld;  // chunk, batch and row strides of part, elements
+  int32_t ksplit;
+  int32_t act;         // ACT_NONE or ACT_GELU
+};
+bool gemm_skinny_chunked_a_supported(const GemmDesc& d, const ChunkedA& a);
+hipError_t launch_gemm_skinny_chunked_a(const GemmDesc& d, const ChunkedA& a, hipStream_t stream);
 
 // Element-guarded GEMM for any dtype, alignment and shape.
 hipError_t launch_gemm_generic(const GemmDesc& d, hipStream_t stream);

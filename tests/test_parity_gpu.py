@@ -328,29 +328,54 @@ def test_skinny_wide_tiles_ragged():
     assert_close(got, oracle.col_linear(x2, w2, N, "gelu"), "skinny wide col gelu")
 
 
-def test_mlp_skinny_wide_tiles_split_k():
-    # Inside tp_mlp the first product may split K: with 96..128 column tiles of
-    # 256 (here 12 per shard x 8 shards, the last one ragged: 3000 columns) it
-    # takes 256-column tiles and two K chunks, the second one short (1000 rows
-    # in chunks of 512), whose sums the finishing pass adds before the GeLU.
-    M, d, width, N = 5, 1000, 3000, 8
-    xi, xf = ints_bf16((M, d), -1, 1, 730, 0)
-    # 128 nonzero columns of X in each K chunk: |H| <= 256, so H is exact in bf16
+# Inside tp_mlp a skinny first product may split K in two; the second product
+# then adds the two fp32 chunk sums (ascending), applies the activation and
+# rounds to bf16 as it loads its token rows, with no finishing pass between.
+# Cases (first product's tiles, second product's tiles, how the sums are laid out):
+#  - shard-major weights, 8 shards: 12 tiles of 256 per shard (the last ragged,
+#    3000 columns), K 1000 in chunks of 512; second product 128 columns wide;
+#    sums one block per shard
+#  - shard-major weights, shards 2..6 of 8 and 3 rows: 120 tiles of 128, two
+#    chunks; sums one block per shard
+#  - one [d, F] weight, 16 shards: 96 tiles of 256 over all shards' columns,
+#    K 3072 in two chunks; second product 256 columns wide (192 tiles); sums
+#    one block holding every shard's columns, at the 16 rows of a full fragment
+CHUNKED_CASES = [(5, 1000, 3000, 8, 0, 8, True), (3, 1000, 3000, 8, 2, 5, True),
+                 (16, 3072, 1536, 16, 0, 16, False)]
+
+
+@pytest.mark.parametrize("M,d,width,N,s0,ns,shard_major", CHUNKED_CASES)
+def test_mlp_skinny_split_k_into_second_product(M, d, width, N, s0, ns, shard_major):
+    seed = 730 + d + M
+    # 256 nonzero columns of X: |H| <= 256, so H is exact in bf16 and the whole chain in fp32
+    xi, xf = ints_bf16((M, d), -1, 1, seed, 0)
     keep = np.zeros(d, dtype=bool)
-    keep[0:128] = keep[600:728] = True
+    keep[:128] = keep[d - 128:] = True
     xi[:, ~keep] = 0
     xf[:, ~keep] = 0
-    w1i, w1f = ints_bf16((d, width * N), -1, 1, 730, 1)
-    w2i, w2f = ints_bf16((width * N, d), -1, 1, 730, 2)
-    note(f"mlp skinny split-K exact M={M} d={d} width={width} N={N}")
-    got = host(tp.mlp(bf16_tensor(xi), bf16_tensor(w1i), bf16_tensor(w2i), N, act="none"))
-    assert_exact(got, oracle.mlp(xf, w1f, w2f, N, "none"), "mlp skinny split-K exact")
-    xb, x = normal_bf16((M, d), 1.0, 731, 0)
-    w1b, w1 = normal_bf16((d, width * N), 0.02, 731, 1)
-    w2b, w2 = normal_bf16((width * N, d), 0.02, 731, 2)
-    note(f"mlp skinny split-K gelu M={M} d={d} width={width} N={N}")
-    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), N))
-    assert_close(got, oracle.mlp(x, w1, w2, N, "gelu"), "mlp skinny split-K gelu")
+    if shard_major:
+        w1i, w1f = ints_bf16((N, d, width), -1, 1, seed, 1)
+        w2i, w2f = ints_bf16((N, width, d), -1, 1, seed, 2)
+        w1full, w2full = np.concatenate(list(w1f), axis=1), np.concatenate(list(w2f), axis=0)
+    else:
+        w1i, w1f = ints_bf16((d, width * N), -1, 1, seed, 1)
+        w2i, w2f = ints_bf16((width * N, d), -1, 1, seed, 2)
+        w1full, w2full = w1f, w2f
+    note(f"mlp skinny split-K exact M={M} d={d} width={width} N={N} s0={s0} ns={ns} shard_major={shard_major}")
+    got = host(tp.mlp(bf16_tensor(xi), bf16_tensor(w1i), bf16_tensor(w2i), N, s0=s0, ns=ns, act="none"))
+    assert_exact(got, oracle.mlp(xf, w1full, w2full, N, "none", s0, ns), "mlp skinny split-K exact")
+
+    xb, x = normal_bf16((M, d), 1.0, seed + 1, 0)
+    if shard_major:
+        w1b, w1 = normal_bf16((N, d, width), 0.02, seed + 1, 1)
+        w2b, w2 = normal_bf16((N, width, d), 0.02, seed + 1, 2)
+        w1full, w2full = np.concatenate(list(w1), axis=1), np.concatenate(list(w2), axis=0)
+    else:
+        w1b, w1full = normal_bf16((d, width * N), 0.02, seed + 1, 1)
+        w2b, w2full = normal_bf16((width * N, d), 0.02, seed + 1, 2)
+    note(f"mlp skinny split-K gelu M={M} d={d} width={width} N={N} s0={s0} ns={ns} shard_major={shard_major}")
+    got = host(tp.mlp(bf16_tensor(xb), bf16_tensor(w1b), bf16_tensor(w2b), N, s0=s0, ns=ns))
+    assert_close(got, oracle.mlp(x, w1full, w2full, N, "gelu", s0, ns), "mlp skinny split-K gelu")
 
 
 # ----------------------------------------------------------------------------- combine kernels
