@@ -332,8 +332,9 @@ def plan(name, t, torch, tp):
         ]
 
         def step(i, rec):
-            # the three calls tp_mlp issues for this shape (its K split stays 1 here),
-            # with events between them; the two weight sets alternate
+            # the three public calls tp_mlp stands for, with events between them
+            # (tp_mlp itself splits the first product's K in two and its second
+            # product reads the chunk sums: decode_mlp_call); the two weight sets alternate
             r = i % 2
             tp.col_linear(t["x"], t["w1s"][r], wl.N, act="gelu", out=h)
             rec()
