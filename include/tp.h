@@ -170,7 +170,8 @@ tp_status tp_reduce_partials(const tp_matrix* P, int32_t n, int32_t axis, const 
  *                                     and tp_row_linear (W2).
  *   Y   [M, Dout], TP_F32, shard_stride 0.
  *   workspace, *workspace_bytes
- *       device scratch for H and the partials (size depends on the shapes).
+ *       device scratch for H, the partials and, for 32 rows or fewer, the
+ *       first product's K-chunk sums (size depends on the shapes).
  *       If workspace is NULL the required size is stored in *workspace_bytes
  *       and TP_OK is returned with nothing enqueued (only shapes, dtypes and
  *       strides are checked then; data pointers may be NULL); otherwise

@@ -340,8 +340,12 @@ def test_skinny_wide_tiles_ragged():
 #  - one [d, F] weight, 16 shards: 96 tiles of 256 over all shards' columns,
 #    K 3072 in two chunks; second product 256 columns wide (192 tiles); sums
 #    one block holding every shard's columns, at the 16 rows of a full fragment
+#  - one token (a single decode step), shard-major weights, 8 shards
+#  - one [d, F] weight, shards 3..12 of 16: 120 tiles of 128, two chunks; sums
+#    one block whose rows are longer than the second product's K
 CHUNKED_CASES = [(5, 1000, 3000, 8, 0, 8, True), (3, 1000, 3000, 8, 2, 5, True),
-                 (16, 3072, 1536, 16, 0, 16, False)]
+                 (16, 3072, 1536, 16, 0, 16, False), (1, 1000, 3000, 8, 0, 8, True),
+                 (7, 3072, 1536, 16, 3, 10, False)]
 
 
 @pytest.mark.parametrize("M,d,width,N,s0,ns,shard_major", CHUNKED_CASES)
