@@ -60,11 +60,19 @@ def test_megatron_step_in_a_graph():
 
 
 def test_decode_and_attention_in_a_graph():
-    # a decode-shaped MLP (skinny kernels, split-K chunk sums in the workspace)
+    # a decode-shaped MLP (skinny kernels, split-K chunk sums in the workspace: K in
+    # four, finished by the chunk-sum pass)
     M, d, F, N = 16, 1024, 4096, 8
     x, w1, w2 = inputs(9300, [(M, d), (d, F), (F, d)], [1.0, 0.02, 0.02])
     y = torch.empty((M, d), dtype=torch.float32, device=dev())
     ws = torch.empty(tp.mlp_workspace_bytes(x, w1, w2, N), dtype=torch.uint8, device=dev())
+    # shard-major weights whose first product splits K in two: the second product
+    # reads the chunk sums itself (12 column tiles of 256 per shard, K 1000)
+    d2, width = 1000, 3000
+    w1s, w2s = inputs(9350, [(N, d2, width), (N, width, d2)], [0.02, 0.02])
+    x2, = inputs(9360, [(M, d2)], [1.0])
+    y2 = torch.empty((M, d2), dtype=torch.float32, device=dev())
+    ws2 = torch.empty(tp.mlp_workspace_bytes(x2, w1s, w2s, N), dtype=torch.uint8, device=dev())
     # causal attention over two sequences, 4 heads x 128 split over 2 shards
     heads, n, dh, L, B = 4, 2, 128, 320, 2
     qkv, = inputs(9400, [(B * L, (heads + 2 * heads) * dh)], [1.0])
@@ -72,6 +80,7 @@ def test_decode_and_attention_in_a_graph():
 
     def step():
         tp.mlp(x, w1, w2, N, out=y, workspace=ws)
+        tp.mlp(x2, w1s, w2s, N, out=y2, workspace=ws2)
         tp.attention(qkv, n, heads, heads, dh, L, True, out=att)
 
     step()
@@ -81,16 +90,18 @@ def test_decode_and_attention_in_a_graph():
         step()
     for r in range(REPLAYS):
         note(f"graph replay {r}")
-        xs, qs = inputs(9500 + r, [(M, d), (B * L, (heads + 2 * heads) * dh)], [1.0, 1.0])
+        xs, qs, x2s = inputs(9500 + r, [(M, d), (B * L, (heads + 2 * heads) * dh), (M, d2)], [1.0, 1.0, 1.0])
         x.copy_(xs)
         qkv.copy_(qs)
+        x2.copy_(x2s)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got_y, got_a = y.clone(), att.clone()
+        got_y, got_y2, got_a = y.clone(), y2.clone(), att.clone()
         step()
         torch.cuda.synchronize()
         assert torch.equal(got_y, y), f"replay {r}: decode MLP differs from eager"
+        assert torch.equal(got_y2, y2), f"replay {r}: decode MLP (chunk sums read by the second product) differs"
         assert torch.equal(got_a, att), f"replay {r}: attention differs from eager"
 
 
